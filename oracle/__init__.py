@@ -165,3 +165,21 @@ def expert_out(wl, x_row, w13, w2, e):
     c = cfg_of(wl)
     lib().orc_expert_out(ctypes.byref(c), _p(x_row), _p(w13), _p(w2), int(e), _p(y))
     return y
+
+
+def permute(wl, ids):
+    """Stable counting sort of slots by segment.  Returns (offsets, sorted_rows, inv_rows);
+    sorted_rows holds -1 past offsets[-1]."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    T = ids.shape[0]
+    KS = wl.top_k + wl.n_shared
+    S = wl.num_experts + wl.n_shared
+    offsets = np.zeros(S + 1, np.int32)
+    sorted_rows = np.full(T * KS, -1, np.int32)
+    inv_rows = np.empty(T * KS, np.int32)
+    c = cfg_of(wl)
+    L = lib()
+    L.orc_permute.argtypes = [ctypes.c_void_p, ctypes.c_int64] + [ctypes.c_void_p] * 4
+    L.orc_permute.restype = None
+    L.orc_permute(ctypes.byref(c), T, _p(ids), _p(offsets), _p(sorted_rows), _p(inv_rows))
+    return offsets, sorted_rows, inv_rows

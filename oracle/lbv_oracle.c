@@ -308,3 +308,57 @@ int orc_moe_forward(const orc_cfg *c, int64_t ntok, const float *x, const uint8_
     }
     return bad ? -1 : 0;
 }
+
+/*
+ * Token copies sorted by expert ([P2] "MoE 实现的源码级要点": tokens are
+ * reordered by expert before the grouped matmuls and restored after).
+ * Plain stable counting sort of the slots by segment.  Slot (t, k), k < K, is
+ * token t's k-th routed choice and belongs to segment ids[t,k]; slot (t, K+j)
+ * belongs to shared segment E + j.  Slot id = t * (K + ns) + k.  An id outside
+ * [0, E), or one already seen earlier in the same token, is not routed
+ * (inv_rows = -1).  offsets [E + ns + 1]; sorted_rows, inv_rows [T (K + ns)].
+ */
+void orc_permute(const orc_cfg *c, int64_t T, const int32_t *ids, int32_t *offsets,
+                 int32_t *sorted_rows, int32_t *inv_rows)
+{
+    const int E = c->num_experts, K = c->top_k, NS = c->n_shared;
+    const int KS = K + NS, S = E + NS;
+    int64_t *count = (int64_t *)calloc(S, sizeof(int64_t));
+    int64_t *fill = (int64_t *)calloc(S, sizeof(int64_t));
+    for (int64_t t = 0; t < T; ++t)
+        for (int k = 0; k < K; ++k) {
+            int e = ids[t * K + k], first = 1;
+            for (int j = 0; j < k; ++j)
+                if (ids[t * K + j] == e) first = 0;
+            if (e >= 0 && e < E && first) count[e]++;
+        }
+    for (int j = 0; j < NS; ++j) count[E + j] = T;
+    offsets[0] = 0;
+    for (int s = 0; s < S; ++s) {
+        offsets[s + 1] = (int32_t)(offsets[s] + count[s]);
+        fill[s] = offsets[s];
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        for (int k = 0; k < K; ++k) {
+            int64_t slot = t * KS + k;
+            int e = ids[t * K + k], first = 1;
+            for (int j = 0; j < k; ++j)
+                if (ids[t * K + j] == e) first = 0;
+            if (e >= 0 && e < E && first) {
+                int64_t pos = fill[e]++;
+                sorted_rows[pos] = (int32_t)slot;
+                inv_rows[slot] = (int32_t)pos;
+            } else {
+                inv_rows[slot] = -1;
+            }
+        }
+        for (int j = 0; j < NS; ++j) {
+            int64_t slot = t * KS + K + j;
+            int64_t pos = fill[E + j]++;
+            sorted_rows[pos] = (int32_t)slot;
+            inv_rows[slot] = (int32_t)pos;
+        }
+    }
+    free(count);
+    free(fill);
+}

@@ -1,0 +1,86 @@
+// Internal declarations shared by the HIP sources of liblbv_moe.
+// Device helpers (bf16 storage, XCD-aware block order, segment lookup) and the
+// launchers that the C ABI in abi.cpp calls after validating its arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lbv {
+
+// ---------------------------------------------------------------------------
+// Problem description resolved on the host from lbv_moe_config.
+// ---------------------------------------------------------------------------
+struct Dims {
+    int64_t T;      // tokens
+    int H;          // hidden
+    int E;          // routed experts
+    int K;          // top_k
+    int NG;         // n_group
+    int TG;         // topk_group
+    int G;          // experts per group
+    int EPL;        // experts per lane in the router (1, 2 or 4)
+    int LG;         // lanes per group in the router (G / EPL, a power of two)
+    int I;          // routed expert width
+    int NS;         // shared pseudo-experts (each of width I)
+    int KS;         // slots per token: K + NS
+    int S;          // segments: E + NS
+    int norm;       // norm_topk_prob
+    float rsf;      // routed_scaling_factor
+    int bf16;       // 1: bf16 storage, 0: fp32 storage
+};
+
+// Launchers (all enqueue on `stream`, return hipGetLastError()).
+hipError_t launch_route(const Dims& d, const void* x, const float* router_w, const float* e_bias,
+                        const uint8_t* mask, int32_t* topk_ids, float* topk_w,
+                        hipStream_t stream);
+
+size_t permute_ws_bytes(const Dims& d);
+hipError_t launch_permute(const Dims& d, const int32_t* topk_ids, int32_t* offsets,
+                          int32_t* sorted_rows, int32_t* inv_rows, void* ws,
+                          hipStream_t stream);
+
+hipError_t launch_gemm_w13(const Dims& d, const void* x, const void* w13,
+                           const void* shared_w13, const int32_t* offsets,
+                           const int32_t* sorted_rows, void* act, hipStream_t stream);
+
+hipError_t launch_gemm_w2(const Dims& d, const void* act, const void* w2, const void* shared_w2,
+                          const int32_t* offsets, void* y, hipStream_t stream);
+
+hipError_t launch_combine(const Dims& d, const void* y, const int32_t* inv_rows,
+                          const float* topk_w, void* out, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+
+// bf16 is stored as its 16-bit pattern.
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16; NaN stays NaN (quiet bit forced).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// Workgroups are handed to the 8 XCDs round-robin (block b runs on XCD b % 8).
+// Renumber them so that each XCD walks a contiguous range of logical tiles:
+// neighbouring tiles (which share operand rows) then meet in the same L2.
+__device__ __forceinline__ int xcd_logical_block(int b, int nblocks) {
+    constexpr int NX = 8;
+    int xcd = b % NX;
+    int idx = b / NX;
+    int base = nblocks / NX;
+    int rem = nblocks % NX;
+    return xcd * base + (xcd < rem ? xcd : rem) + idx;
+}
+
+}  // namespace lbv

@@ -1,0 +1,368 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bar: expert ids equal as sets on every token whose decision margins exceed
+1e-5 (near ties may differ only by a near-equal choice), routing weights within
+1e-5 relative, permutation bit-exact, and outputs within relative Frobenius
+error 5e-3 and max-abs 3e-2 for bf16 storage (bf16 operands, fp32
+accumulation), 1e-5 / 1e-5 for fp32 storage (fp32 everywhere; the error is
+fp32 accumulation order over H <= 2048 terms, ~1e-6 relative).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import routed_moe_dit_amd as lbv
+import synth
+from gpu_util import cfg_for, compare_routing, dev, forward, host, metrics, note, upload
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+BF16_TOL = dict(rel_frob=5e-3, max_abs=3e-2)
+F32_TOL = dict(rel_frob=1e-5, max_abs=1e-5)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    lbv.load()          # the HIP library must be present: no fallback exists
+    yield
+
+
+def var(name, **kw):
+    base = dict(name=name, T=200, hidden=512, num_experts=64, n_group=4, topk_group=2, top_k=6,
+                intermediate=128, n_shared=1, dtype="bf16", seed=11, b_std=0.1)
+    base.update(kw)
+    base.setdefault("wr_std", base["hidden"] ** -0.5)
+    return synth.Workload(**base)
+
+
+ROUTE_CASES = [
+    W[0], W[1], W[2],
+    var("E256_ng8_EPL4", num_experts=256, n_group=8, topk_group=4, top_k=8, T=333, hidden=256),
+    var("E64_ng2_tg1", num_experts=64, n_group=2, topk_group=1, top_k=6, T=100, hidden=128),
+    var("E8_G2_f32", num_experts=8, n_group=4, topk_group=2, top_k=2, T=65, hidden=64,
+        dtype="f32"),
+    var("E16_plain_T1", num_experts=16, n_group=1, topk_group=1, top_k=5, T=1, hidden=64),
+    var("nonorm_negbias", norm_topk_prob=False, b_std=1.0, T=130),
+]
+
+
+def run_route(wl, d):
+    cfg = cfg_for(wl)
+    T = d["x"].shape[0]
+    ids = torch.empty(T, wl.top_k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, wl.top_k, dtype=torch.float32, device="cuda")
+    lbv.lbv_moe_route(cfg, d["x"], d["router_w"], d["e_bias"], d["mask"], ids, w)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), w.cpu().numpy()
+
+
+@pytest.mark.parametrize("wl", ROUTE_CASES, ids=lambda w: w.name)
+def test_route_parity(wl):
+    note("route %s" % wl.name)
+    inp = synth.make_inputs(wl)
+    d = upload(wl, inp)
+    g_ids, g_w = run_route(wl, d)
+    o = oracle.route(wl, inp["x"], inp["router_w"], inp["e_bias"], inp["mask"])
+    same, near = compare_routing(g_ids, g_w, o)
+    if inp["mask"] is not None:
+        pad = inp["mask"] == 0
+        assert (g_ids[pad] == -1).all() and (g_w[pad] == 0).all()
+        assert (g_ids[~pad] >= 0).all()
+    # every chosen expert lies in a kept group: at most topk_group distinct groups
+    G = wl.num_experts // wl.n_group
+    for row in g_ids[g_ids[:, 0] >= 0]:
+        assert len(set(row.tolist())) == wl.top_k
+        assert len({e // G for e in row.tolist()}) <= wl.topk_group
+    print("route %s: near-tie tokens %d, mismatched %d" % (wl.name, near.sum(), (~same).sum()))
+
+
+@pytest.mark.parametrize("wl", [W[3], W[4]], ids=lambda w: w.name)
+def test_route_parity_full_size(wl):
+    note("route full %s" % wl.name)
+    inp = synth.make_inputs(wl)
+    d = dict(x=dev(inp["x"], "bf16"), router_w=dev(inp["router_w"], "f32"),
+             e_bias=dev(inp["e_bias"], "f32"), mask=None)
+    g_ids, g_w = run_route(wl, d)
+    o = oracle.route(wl, inp["x"], inp["router_w"], inp["e_bias"])
+    same, near = compare_routing(g_ids, g_w, o)
+    print("route %s: near-tie %d of %d, mismatched %d" % (wl.name, near.sum(), wl.T, (~same).sum()))
+
+
+@pytest.mark.parametrize("T,E,K,ns", [(1, 16, 4, 1), (255, 128, 8, 1), (256, 128, 8, 1),
+                                      (257, 128, 8, 0), (1000, 64, 6, 2), (38000, 128, 8, 1)])
+def test_permute_parity(T, E, K, ns):
+    note("permute T=%d E=%d K=%d ns=%d" % (T, E, K, ns))
+    wl = var("perm", T=T, num_experts=E, top_k=K, n_shared=ns, n_group=4, topk_group=4)
+    rng = np.random.default_rng(T + E)
+    # skewed choices like the hot-expert workload, plus unrouted and repeated ids
+    p = rng.dirichlet(np.full(E, 0.3))
+    ids = np.stack([rng.choice(E, K, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    ids[::5, -1] = -1
+    ids[3::13, 1 % K] = ids[3::13, 0]
+    cfg = cfg_for(wl)
+    ids_d = torch.from_numpy(ids).cuda()
+    S, KS = E + ns, K + ns
+    off = torch.full((S + 1,), -7, dtype=torch.int32, device="cuda")
+    srt = torch.full((T * KS,), -7, dtype=torch.int32, device="cuda")
+    inv = torch.full((T * KS,), -7, dtype=torch.int32, device="cuda")
+    ws = torch.empty(lbv.lbv_moe_permute_workspace_size(cfg, T), dtype=torch.uint8, device="cuda")
+    lbv.lbv_moe_permute(cfg, ids_d, off, srt, inv, ws)
+    torch.cuda.synchronize()
+    o_off, o_srt, o_inv = oracle.permute(wl, ids)
+    R = int(o_off[-1])
+    np.testing.assert_array_equal(off.cpu().numpy(), o_off)
+    np.testing.assert_array_equal(srt.cpu().numpy()[:R], o_srt[:R])
+    np.testing.assert_array_equal(inv.cpu().numpy(), o_inv)
+
+
+
+
+def ref_act(wl, inp, off, srt, r):
+    KS = wl.top_k + wl.n_shared
+    t, k = divmod(int(srt[r]), KS)
+    seg = int(np.searchsorted(off, r, side="right") - 1)
+    if seg < wl.num_experts:
+        return oracle.expert_act(wl, inp["x"][t], inp["w13"], seg)
+    j = seg - wl.num_experts
+    I = wl.intermediate
+    return oracle.shared_act(wl, inp["x"][t], inp["shared_w13"])[j * I:(j + 1) * I]
+
+
+@pytest.mark.parametrize("wl", [W[0], W[1], var("ns2_ragged", n_shared=2, T=77)],
+                         ids=lambda w: w.name)
+def test_gemm_w13_silu_parity(wl):
+    """act rows against the oracle's SwiGLU, on the oracle's own routing."""
+    note("gemm_w13 %s" % wl.name)
+    inp = synth.make_inputs(wl)
+    d = upload(wl, inp)
+    o = oracle.route(wl, inp["x"], inp["router_w"], inp["e_bias"], inp["mask"])
+    off, srt, inv = oracle.permute(wl, o["ids"])
+    R = int(off[-1])
+    cfg = cfg_for(wl)
+    act = torch.zeros(wl.T * (wl.top_k + wl.n_shared), wl.intermediate,
+                      dtype=d["x"].dtype, device="cuda")
+    lbv.lbv_moe_gemm_w13_silu(cfg, d["x"], d["w13"], d["shared_w13"],
+                              torch.from_numpy(off).cuda(), torch.from_numpy(srt).cuda(), act)
+    torch.cuda.synchronize()
+    g = host(act)
+    rng = np.random.default_rng(0)
+    rows = np.arange(R) if R <= 400 else np.unique(np.concatenate(
+        [rng.choice(R, 300, replace=False), off[:-1][np.diff(off) > 0], off[1:] - 1]))
+    rows = rows[rows < R]
+    ref = np.stack([ref_act(wl, inp, off, srt, r) for r in rows])
+    got = g[rows]
+    m = metrics(got, ref)
+    print("gemm_w13 %s: %s" % (wl.name, m))
+    if wl.dtype == "bf16":
+        # one bf16 rounding of act: |err| <= 2^-8 |act| plus accumulation noise
+        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-4 * np.abs(ref).max())
+    else:
+        assert m["rel_frob"] <= 1e-5
+    # rows past R are untouched
+    assert np.all(g[R:] == 0)
+
+
+def test_gemm_w2_combine_parity():
+    """Down projection + combine on oracle act rows (bf16-rounded) for sampled tokens."""
+    wl = W[1]
+    note("gemm_w2_combine %s" % wl.name)
+    inp = synth.make_inputs(wl)
+    d = upload(wl, inp)
+    o = oracle.route(wl, inp["x"], inp["router_w"], inp["e_bias"])
+    off, srt, inv = oracle.permute(wl, o["ids"])
+    KS = wl.top_k + wl.n_shared
+    toks = np.random.default_rng(5).choice(wl.T, 24, replace=False)
+    act = np.zeros((wl.T * KS, wl.intermediate), np.float32)
+    for t in toks:
+        for k in range(KS):
+            r = inv[t * KS + k]
+            act[r] = ref_act(wl, inp, off, srt, r)
+    synth.round_to_bf16(act)
+    cfg = cfg_for(wl)
+    out = torch.zeros(wl.T, wl.hidden, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(lbv.lbv_moe_w2_workspace_size(cfg, wl.T), dtype=torch.uint8, device="cuda")
+    lbv.lbv_moe_gemm_w2_combine(cfg, dev(act, "bf16"), d["w2"], d["shared_w2"],
+                                torch.from_numpy(off).cuda(), torch.from_numpy(srt).cuda(),
+                                torch.from_numpy(inv).cuda(), torch.from_numpy(o["w"]).cuda(),
+                                out, ws)
+    torch.cuda.synchronize()
+    ref = oracle.moe_forward(wl, inp["x"][toks], inp["router_w"], inp["e_bias"], inp["w13"],
+                             inp["w2"], inp["shared_w13"], inp["shared_w2"])
+    m = metrics(host(out)[toks], ref["out"])
+    print("gemm_w2_combine: %s" % m)
+    assert m["rel_frob"] <= BF16_TOL["rel_frob"] and m["max_abs"] <= BF16_TOL["max_abs"]
+
+
+FWD_CASES = [
+    W[0], W[1],
+    var("ns0", n_shared=0, T=97),
+    var("ns2", n_shared=2, T=64),
+    var("K1", top_k=1, topk_group=1, T=50),
+    var("E256_EPL4", num_experts=256, n_group=8, topk_group=4, top_k=8, T=40, hidden=256),
+    var("nonorm", norm_topk_prob=False, T=60),
+    var("T1", T=1),
+    var("f32_ragged", dtype="f32", T=45, hidden=128, intermediate=64),
+]
+
+
+def check_forward(wl, inp, out, ids, w, rows=None, tol=None):
+    rows = np.arange(wl.T) if rows is None else rows
+    mask = None if inp["mask"] is None else inp["mask"][rows]
+    ref = oracle.moe_forward(wl, inp["x"][rows], inp["router_w"], inp["e_bias"], inp["w13"],
+                             inp["w2"], inp["shared_w13"], inp["shared_w2"], mask)
+    same, near = compare_routing(ids.cpu().numpy()[rows], w.cpu().numpy()[rows], ref)
+    got = host(out)[rows]
+    m = metrics(got[same], ref["out"][same])
+    tol = tol or (BF16_TOL if wl.dtype == "bf16" else F32_TOL)
+    print("forward %s: %s near-tie %d mismatched %d" % (wl.name, m, near.sum(), (~same).sum()))
+    assert m["finite"]
+    assert m["rel_frob"] <= tol["rel_frob"], m
+    assert m["max_abs"] <= tol["max_abs"], m
+    return m
+
+
+@pytest.mark.parametrize("wl", FWD_CASES, ids=lambda w: w.name)
+def test_forward_parity(wl):
+    note("forward %s" % wl.name)
+    inp = synth.make_inputs(wl)
+    d = upload(wl, inp)
+    out, ids, w = forward(wl, d)
+    check_forward(wl, inp, out, ids, w)
+
+
+def test_forward_parity_padded_batch():
+    """CFG batch B=2 with 40 padding tokens: sampled rows incl. every padding row."""
+    wl = W[2]
+    note("forward %s" % wl.name)
+    inp = synth.make_inputs(wl)
+    d = upload(wl, inp)
+    out, ids, w = forward(wl, d)
+    rng = np.random.default_rng(2)
+    rows = np.unique(np.concatenate([rng.choice(1560, 200, replace=False), np.arange(1560, 1600),
+                                     [0, 799, 800, 1559]]))
+    check_forward(wl, inp, out, ids, w, rows)
+    pad = inp["mask"] == 0
+    assert (ids.cpu().numpy()[pad] == -1).all()
+
+
+@pytest.mark.parametrize("wl", [W[3], W[4]], ids=lambda w: w.name)
+def test_forward_parity_full_size(wl):
+    """38,000 tokens in one call; the oracle checks 64 sampled tokens."""
+    note("forward full %s" % wl.name)
+    inp = synth.make_inputs(wl)
+    d = upload(wl, inp)
+    out, ids, w = forward(wl, d)
+    rows = np.unique(np.concatenate([np.random.default_rng(wl.seed).choice(wl.T, 62, replace=False),
+                                     [0, wl.T - 1]]))
+    check_forward(wl, inp, out, ids, w, rows)
+    counts = np.bincount(ids.cpu().numpy().reshape(-1), minlength=wl.num_experts)
+    if wl.hot:
+        print("hot-expert share of assignments: %.3f" % (counts[list(wl.hot)].sum() / counts.sum()))
+
+
+def test_sample_isolation_bitwise():
+    """A sample's outputs inside the B=2 batch equal those of the sample alone."""
+    wl = W[2]
+    note("isolation %s" % wl.name)
+    inp = synth.make_inputs(wl)
+    d = upload(wl, inp)
+    out, ids, w = forward(wl, d)
+    for lo, hi in ((0, 800), (800, 1600)):
+        x1 = d["x"][lo:hi].contiguous()
+        m1 = d["mask"][lo:hi].contiguous()
+        o1, i1, w1 = forward(wl, d, x=x1, mask=m1)
+        assert torch.equal(o1, out[lo:hi]) and torch.equal(i1, ids[lo:hi]) and torch.equal(w1, w[lo:hi])
+    perm = torch.randperm(1600, generator=torch.Generator().manual_seed(0)).cuda()
+    op, ip, _ = forward(wl, d, x=d["x"][perm].contiguous(), mask=d["mask"][perm].contiguous())
+    assert torch.equal(op, out[perm]) and torch.equal(ip, ids[perm])
+
+
+def test_determinism_and_split_calls():
+    """Two forwards are bitwise equal, and so is the chain of the four calls."""
+    wl = W[1]
+    note("determinism %s" % wl.name)
+    inp = synth.make_inputs(wl)
+    d = upload(wl, inp)
+    o1, i1, w1 = forward(wl, d)
+    o2, i2, w2 = forward(wl, d)
+    assert torch.equal(o1, o2) and torch.equal(i1, i2) and torch.equal(w1, w2)
+    cfg = cfg_for(wl)
+    T, K, KS, S = wl.T, wl.top_k, wl.top_k + wl.n_shared, wl.num_experts + wl.n_shared
+    ids = torch.empty(T, K, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, K, dtype=torch.float32, device="cuda")
+    lbv.lbv_moe_route(cfg, d["x"], d["router_w"], d["e_bias"], None, ids, w)
+    off = torch.empty(S + 1, dtype=torch.int32, device="cuda")
+    srt = torch.empty(T * KS, dtype=torch.int32, device="cuda")
+    inv = torch.empty(T * KS, dtype=torch.int32, device="cuda")
+    pws = torch.empty(lbv.lbv_moe_permute_workspace_size(cfg, T), dtype=torch.uint8, device="cuda")
+    lbv.lbv_moe_permute(cfg, ids, off, srt, inv, pws)
+    act = torch.empty(T * KS, wl.intermediate, dtype=torch.bfloat16, device="cuda")
+    lbv.lbv_moe_gemm_w13_silu(cfg, d["x"], d["w13"], d["shared_w13"], off, srt, act)
+    out = torch.empty(T, wl.hidden, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(lbv.lbv_moe_w2_workspace_size(cfg, T), dtype=torch.uint8, device="cuda")
+    lbv.lbv_moe_gemm_w2_combine(cfg, act, d["w2"], d["shared_w2"], off, srt, inv, w, out, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o1) and torch.equal(ids, i1) and torch.equal(w, w1)
+
+
+def test_bias_selects_but_does_not_weigh():
+    """Expert 3 forced into every set by its bias; weights stay functions of the
+    raw scores: equal bitwise wherever the slot order did not change."""
+    wl = var("bias", T=256)
+    note("bias invariant")
+    inp = synth.make_inputs(wl)
+    d = upload(wl, inp)
+    i1, w1 = run_route(wl, d)
+    d2 = dict(d)
+    b2 = inp["e_bias"].copy()
+    b2[3] += 10.0
+    d2["e_bias"] = torch.from_numpy(b2).cuda()
+    i2, w2 = run_route(wl, d2)
+    assert (i2 == 3).any(1).all()
+    sameorder = (i1 == i2).all(1)
+    assert np.array_equal(w1[sameorder], w2[sameorder])
+    o2 = oracle.route(wl, inp["x"], inp["router_w"], b2)
+    compare_routing(i2, w2, o2)
+
+
+def test_scaling_applied_once():
+    """Identical routed experts, no shared expert: out = 2.5 f(x) (not 6.25 f(x))."""
+    wl = var("scale", T=32, n_shared=0)
+    note("scaling once")
+    inp = synth.make_inputs(wl)
+    inp["w13"][:] = inp["w13"][:1]
+    inp["w2"][:] = inp["w2"][:1]
+    d = upload(wl, inp)
+    out, ids, w = forward(wl, d)
+    f = np.stack([oracle.expert_out(wl, inp["x"][t], inp["w13"], inp["w2"], 0) for t in range(32)])
+    m = metrics(host(out), 2.5 * f)
+    assert m["rel_frob"] <= 5e-3, m
+
+
+def test_all_padding_gives_shared_only():
+    wl = var("allpad", T=70)
+    note("all padding")
+    inp = synth.make_inputs(wl)
+    inp["mask"] = np.zeros(70, np.uint8)
+    d = upload(wl, inp)
+    out, ids, w = forward(wl, d)
+    assert (ids.cpu().numpy() == -1).all() and (w.cpu().numpy() == 0).all()
+    check_forward(wl, inp, out, ids, w)
+
+
+def test_zero_tokens_is_noop():
+    wl = W[1]
+    cfg = cfg_for(wl)
+    x = torch.empty(0, wl.hidden, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    lbv.lbv_moe_forward(cfg, x, None, torch.empty(128, 2048, device="cuda"),
+                        torch.empty(128, device="cuda"),
+                        torch.empty(1, dtype=torch.bfloat16, device="cuda"),
+                        torch.empty(1, dtype=torch.bfloat16, device="cuda"), None, None,
+                        torch.empty(0, wl.hidden, dtype=torch.bfloat16, device="cuda"), None, None,
+                        ws)
+    torch.cuda.synchronize()
