@@ -37,22 +37,24 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, defines=(), lib: str = LIB, build_dir: str = BUILD) -> str:
+    """Compile every source and link ``lib``; ``defines`` are extra -D options."""
+    os.makedirs(build_dir, exist_ok=True)
+    extra = ["-D" + d for d in defines]
 
     def one(src):
-        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        out = _run([HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+        out = _run([HIPCC] + FLAGS + extra + ["-c", os.path.join(CSRC, src), "-o", obj])
         if verbose and out.strip():
             print(out)
         return obj
 
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(one, SOURCES))
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -26,6 +26,8 @@
 // For the gate/up matmul a B tile holds BN/2 gate rows and the matching BN/2
 // up rows, and each wave's accumulators for gate column n and up column n sit
 // in the same lane and register, so silu(g) * u is formed in registers.
+#include <type_traits>
+
 #include "lbv_internal.h"
 
 namespace lbv {
@@ -94,22 +96,76 @@ __device__ bool find_tile(const GemmArgs& a, int BM, int mt, int* seg_out, int* 
     return true;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int MODE>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
-    static_assert(WM * WN == 4, "4 waves");
-    static_assert(BK == 64, "LDS swizzle assumes 8 chunks of 16 B per row");
-    constexpr int TM = BM / (WM * 32);
-    constexpr int TN = BN / (WN * 32);
-    static_assert(TM >= 1 && TN >= 1, "tile");
-    static_assert(MODE == 1 || TN % 2 == 0, "gate/up tiles come in pairs");
-    constexpr int A_ELEMS = BM * BK, B_ELEMS = BN * BK;
-    constexpr int AR = BM / 32, BR = BN / 32;   // load rounds (32 rows per round)
+// Waits until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
 
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (A_ELEMS + B_ELEMS)];
+// Workgroup barrier without the memory fence that __syncthreads() implies (the
+// fence would wait for every load in flight, i.e. drain the prefetch queue).
+// The empty asm keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void block_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Asynchronous 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4):
+// lane l's 16 bytes land at LDS byte address lds_base + 16 l.  Written as asm
+// so that the compiler's wait-count pass, which cannot tell the stage being
+// filled from the stage being read, does not drain the queue before every LDS
+// read; the kernel orders these copies itself (wait_vmcnt + block_barrier).
+// The instruction has no register results.
+__device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t lds_base) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off"
+        :
+        : "s"(lds_base), "v"(gsrc)
+        : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)p));
+}
+
+// 16-byte chunk swizzle of a 64-byte LDS row (4 chunks): chunk c of row r is
+// stored at c ^ ((r >> 2) & 3).  Measured on gfx950 for the fragment read
+// (lanes 0-31 rows r0 + lane, lanes 32-63 the next chunk): ~209 B/clk/CU, i.e.
+// conflict-free, against ~62 B/clk unswizzled and ~120 B/clk for
+// c ^ ((r >> 1) & 3).
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+
+template <int BM, int BN, int MODE>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
+    constexpr int BK = 32;                       // bf16 per row per stage (64 bytes)
+    constexpr int STAGES = 4;                    // LDS ring: STAGES-1 k-tiles in flight
+    constexpr int TM = BM / 64;                  // token tiles (32 rows) per wave
+    constexpr int TN = BN / 64;                  // weight-row tiles (32 rows) per wave
+    static_assert(MODE == 1 || TN % 2 == 0, "gate/up tiles come in pairs");
+    constexpr int STAGE = (BM + BN) * BK;        // bf16 elements per stage
+    constexpr int AI = BM / 64, BI = BN / 64;    // 1 KB load instructions per wave per stage
+    constexpr int NI = AI + BI;
+
+    // Four distinct LDS objects (not one array indexed by kt % 4): with the
+    // stage named at compile time the compiler can prove that a stage being
+    // read is not one being filled by the asynchronous loads, and does not
+    // drain the whole load queue before every LDS read.
+    __shared__ __attribute__((aligned(1024))) uint16_t lds0[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds1[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds2[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds3[STAGE];
     __shared__ int s_tmp[8];
     __shared__ int s_sel[2];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lid = xcd_logical_block(blockIdx.x, gridDim.x);
     const int mt = lid / a.ntn;
     const int nt = lid % a.ntn;
@@ -118,37 +174,38 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
 
     const int seg_r0 = a.offsets[seg];
     const int seg_n = a.offsets[seg + 1] - seg_r0;
-    const int kdim = a.kdim;
     const bool shared_seg = seg >= a.E;
     const int jsh = seg - a.E;
     const int Is = a.NS * a.I;
 
-    // ---- per-thread global row pointers --------------------------------------
-    const int lrow = tid >> 3;        // row within a 32-row round
-    const int lchunk = tid & 7;       // 16-byte chunk within the 128-byte row slice
-    const uint16_t* aptr[AR];
-    const uint16_t* bptr[BR];
+    // ---- global source of each lane's 16-byte chunk (per load instruction) ----
+    // Instruction i of wave w fills LDS rows w*(rows/4) + 16 i + [0, 16) of the
+    // stage; lane l lands at row +l/4, physical chunk l%4, which holds logical
+    // chunk (l%4) ^ swz(row).
+    const uint16_t* aptr[AI];
+    const uint16_t* bptr[BI];
 #pragma unroll
-    for (int r = 0; r < AR; ++r) {
-        int m = m0 + r * 32 + lrow;
+    for (int i = 0; i < AI; ++i) {
+        const int r = wave * (BM / 4) + i * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ swz(r);
+        int m = m0 + r;
         if (m >= seg_n) m = seg_n - 1;
         if (MODE == 0) {
-            int slot = a.rows[seg_r0 + m];
-            int64_t tok = slot / a.KS;
-            if (tok < 0) tok = 0;
-            if (tok >= a.T) tok = a.T - 1;
-            aptr[r] = static_cast<const uint16_t*>(a.A) + tok * a.H + lchunk * 8;
+            int64_t tok = a.rows[seg_r0 + m] / a.KS;
+            tok = tok < 0 ? 0 : (tok >= a.T ? a.T - 1 : tok);
+            aptr[i] = static_cast<const uint16_t*>(a.A) + tok * a.H + c * 8;
         } else {
-            aptr[r] = static_cast<const uint16_t*>(a.A) + static_cast<int64_t>(seg_r0 + m) * a.I +
-                      lchunk * 8;
+            aptr[i] = static_cast<const uint16_t*>(a.A) + static_cast<int64_t>(seg_r0 + m) * a.I +
+                      c * 8;
         }
     }
 #pragma unroll
-    for (int r = 0; r < BR; ++r) {
-        const int br = r * 32 + lrow;    // B tile row
+    for (int i = 0; i < BI; ++i) {
+        const int r = wave * (BN / 4) + i * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ swz(r);
         if (MODE == 0) {
-            const int half = br / (BN / 2);
-            int n = nt * (BN / 2) + (br % (BN / 2));
+            const int half = r / (BN / 2);
+            int n = nt * (BN / 2) + (r % (BN / 2));
             if (n >= a.I) n = a.I - 1;
             int64_t row;
             const uint16_t* base;
@@ -159,120 +216,133 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
                 base = static_cast<const uint16_t*>(a.Bsh);
                 row = half ? Is + jsh * a.I + n : jsh * a.I + n;
             }
-            bptr[r] = base + row * a.H + lchunk * 8;
+            bptr[i] = base + row * a.H + c * 8;
         } else {
-            int n = nt * BN + br;
+            int n = nt * BN + r;
             if (n >= a.H) n = a.H - 1;
-            if (!shared_seg)
-                bptr[r] = static_cast<const uint16_t*>(a.B) + static_cast<int64_t>(seg) * a.H * a.I +
-                          static_cast<int64_t>(n) * a.I + lchunk * 8;
-            else
-                bptr[r] = static_cast<const uint16_t*>(a.Bsh) + static_cast<int64_t>(n) * Is +
-                          jsh * a.I + lchunk * 8;
+            bptr[i] = shared_seg
+                ? static_cast<const uint16_t*>(a.Bsh) + static_cast<int64_t>(n) * Is + jsh * a.I + c * 8
+                : static_cast<const uint16_t*>(a.B) + static_cast<int64_t>(seg) * a.H * a.I +
+                      static_cast<int64_t>(n) * a.I + c * 8;
         }
     }
+    const int a_lds = wave * (BM / 4) * BK;          // element offsets inside a stage
+    const int b_lds = BM * BK + wave * (BN / 4) * BK;
 
-    // ---- LDS addressing (swizzled 16-byte chunks) ------------------------------
-    // store: row lrow + 32 r, chunk lchunk  -> element offset
-    const int st_off = lrow * BK + ((lchunk ^ (lrow & 7)) * 8);   // (r*32 + lrow) & 7 == lrow & 7
+    auto stage_buf = [&](auto S) -> uint16_t* {
+        if constexpr (decltype(S)::value == 0) return lds0;
+        else if constexpr (decltype(S)::value == 1) return lds1;
+        else if constexpr (decltype(S)::value == 2) return lds2;
+        else return lds3;
+    };
+    auto issue = [&](auto S, int kt) {     // k-tile kt into stage S
+        const int k0 = kt * BK;
+        uint16_t* st = stage_buf(S);
+        const uint32_t base = lds_addr(st);
+#pragma unroll
+        for (int i = 0; i < AI; ++i)
+            lds_dma16(aptr[i] + k0, base + (a_lds + i * 16 * BK) * 2);
+#pragma unroll
+        for (int i = 0; i < BI; ++i)
+            lds_dma16(bptr[i] + k0, base + (b_lds + i * 16 * BK) * 2);
+    };
 
-    u32x4 ra[AR], rb[BR];
-
-    // ---- wave tile ----------------------------------------------------------------
-    const int wm = wave / WN, wn = wave % WN;
-    f32x16 acc[TM][TN];
+    // ---- fragments: weight rows are the MFMA's first operand, token rows the
+    // second, so each lane ends up with 4 consecutive output columns ----------
+    const int wm = wave >> 1, wn = wave & 1;
+    int trow[TM], wrow[TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-
-    // fragment rows in LDS
-    int arow[TM], brow[TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) arow[i] = wm * TM * 32 + i * 32 + (lane & 31);
+    for (int i = 0; i < TM; ++i) trow[i] = wm * (BM / 2) + i * 32 + (lane & 31);
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
         if (MODE == 0) {
             constexpr int HT = TN / 2;
-            if (j < HT) brow[j] = wn * HT * 32 + j * 32 + (lane & 31);
-            else brow[j] = BN / 2 + wn * HT * 32 + (j - HT) * 32 + (lane & 31);
+            wrow[j] = (j < HT ? 0 : BN / 2) + wn * (BN / 4) + (j % HT) * 32 + (lane & 31);
         } else {
-            brow[j] = wn * TN * 32 + j * 32 + (lane & 31);
+            wrow[j] = wn * (BN / 2) + j * 32 + (lane & 31);
         }
     }
     const int khalf = lane >> 5;
 
-    const int nk = kdim / BK;
-    // prologue: k-tile 0 -> registers -> LDS buffer 0
+    f32x16 acc[TN][TM];
 #pragma unroll
-    for (int r = 0; r < AR; ++r) ra[r] = *reinterpret_cast<const u32x4*>(aptr[r]);
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-    for (int r = 0; r < BR; ++r) rb[r] = *reinterpret_cast<const u32x4*>(bptr[r]);
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int r = 0; r < AR; ++r) *reinterpret_cast<u32x4*>(smem + r * 32 * BK + st_off) = ra[r];
-#pragma unroll
-    for (int r = 0; r < BR; ++r)
-        *reinterpret_cast<u32x4*>(smem + A_ELEMS + r * 32 * BK + st_off) = rb[r];
-    __syncthreads();
+            for (int q = 0; q < 16; ++q) acc[j][i][q] = 0.f;
 
-    for (int kt = 0; kt < nk; ++kt) {
-        const bool more = kt + 1 < nk;
-        if (more) {   // next k-tile's global loads stay in flight during the MFMAs
-            const int k0 = (kt + 1) * BK;
-#pragma unroll
-            for (int r = 0; r < AR; ++r) ra[r] = *reinterpret_cast<const u32x4*>(aptr[r] + k0);
-#pragma unroll
-            for (int r = 0; r < BR; ++r) rb[r] = *reinterpret_cast<const u32x4*>(bptr[r] + k0);
-        }
-        const uint16_t* As = smem + (kt & 1) * (A_ELEMS + B_ELEMS);
-        const uint16_t* Bs = As + A_ELEMS;
+    const int nk = a.kdim / BK;
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
+    issue(S0{}, 0);
+    if (1 < nk) issue(S1{}, 1);
+    if (2 < nk) issue(S2{}, 2);
+
+    // one k-tile: wait for its stage, free the previous stage, refill it with
+    // k-tile kt + 3, multiply
+    auto step = [&](auto S, int kt) {
+        constexpr int SI = decltype(S)::value;
+        const int ahead = nk - 1 - kt;            // k-tiles issued after kt
+        if (ahead >= STAGES - 2) wait_vmcnt<(STAGES - 2) * NI>();
+        else if (ahead == 1) wait_vmcnt<NI>();
+        else wait_vmcnt<0>();
+        block_barrier();
+        if (kt + STAGES - 1 < nk) issue(std::integral_constant<int, (SI + 3) % 4>{}, kt + STAGES - 1);
+        const uint16_t* As = stage_buf(S);
+        const uint16_t* Bs = As + BM * BK;
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
             const int ch = kk * 2 + khalf;
-            bf16x8 af[TM], bfr[TN];
+            bf16x8 tf[TM], wf[TN];
 #pragma unroll
             for (int i = 0; i < TM; ++i)
-                af[i] = *reinterpret_cast<const bf16x8*>(As + arow[i] * BK + ((ch ^ (arow[i] & 7)) * 8));
+                tf[i] = *reinterpret_cast<const bf16x8*>(As + trow[i] * BK + ((ch ^ swz(trow[i])) * 8));
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + brow[j] * BK + ((ch ^ (brow[j] & 7)) * 8));
+                wf[j] = *reinterpret_cast<const bf16x8*>(Bs + wrow[j] * BK + ((ch ^ swz(wrow[j])) * 8));
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
+            for (int j = 0; j < TN; ++j)
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                for (int i = 0; i < TM; ++i)
+                    acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], tf[i], acc[j][i], 0, 0, 0);
         }
-        if (more) {
-            uint16_t* An = smem + ((kt + 1) & 1) * (A_ELEMS + B_ELEMS);
-#pragma unroll
-            for (int r = 0; r < AR; ++r) *reinterpret_cast<u32x4*>(An + r * 32 * BK + st_off) = ra[r];
-#pragma unroll
-            for (int r = 0; r < BR; ++r)
-                *reinterpret_cast<u32x4*>(An + A_ELEMS + r * 32 * BK + st_off) = rb[r];
-        }
-        __syncthreads();
+    };
+    for (int kt = 0; kt < nk; kt += 4) {
+        step(S0{}, kt);
+        if (kt + 1 < nk) step(S1{}, kt + 1);
+        if (kt + 2 < nk) step(S2{}, kt + 2);
+        if (kt + 3 < nk) step(S3{}, kt + 3);
     }
 
-    // ---- epilogue -------------------------------------------------------------------
+    // ---- epilogue: lane holds columns 8q + 4*khalf + [0,4) of row (lane & 31) ----
     uint16_t* C = static_cast<uint16_t*>(a.C);
     if (MODE == 0) {
         constexpr int HT = TN / 2;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
+            const int m = m0 + wm * (BM / 2) + i * 32 + (lane & 31);
+            if (m >= seg_n) continue;
+            uint16_t* crow = C + static_cast<int64_t>(seg_r0 + m) * a.I;
 #pragma unroll
             for (int j = 0; j < HT; ++j) {
-                const int col = nt * (BN / 2) + wn * HT * 32 + j * 32 + (lane & 31);
 #pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const int row = wm * TM * 32 + i * 32 + 8 * (q >> 2) + 4 * khalf + (q & 3);
-                    const int m = m0 + row;
-                    if (m < seg_n && col < a.I) {
-                        const float g = acc[i][j][q];
-                        const float u = acc[i][j + HT][q];
-                        const float v = g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-                        C[static_cast<int64_t>(seg_r0 + m) * a.I + col] = f32_to_bf16(v);
+                for (int q = 0; q < 4; ++q) {
+                    const int col = nt * (BN / 2) + wn * (BN / 4) + j * 32 + 8 * q + 4 * khalf;
+                    float v[4];
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        const float g = acc[j][i][4 * q + p];
+                        const float u = acc[j + HT][i][4 * q + p];
+                        v[p] = g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+                    }
+                    if (col < a.I) {
+                        uint2 o;
+                        o.x = pack_bf16x2(v[0], v[1]);
+                        o.y = pack_bf16x2(v[2], v[3]);
+                        *reinterpret_cast<uint2*>(crow + col) = o;
                     }
                 }
             }
@@ -280,15 +350,20 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     } else {
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
+            const int m = m0 + wm * (BM / 2) + i * 32 + (lane & 31);
+            if (m >= seg_n) continue;
+            uint16_t* crow = C + static_cast<int64_t>(seg_r0 + m) * a.H;
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
-                const int col = nt * BN + wn * TN * 32 + j * 32 + (lane & 31);
 #pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const int row = wm * TM * 32 + i * 32 + 8 * (q >> 2) + 4 * khalf + (q & 3);
-                    const int m = m0 + row;
-                    if (m < seg_n && col < a.H)
-                        C[static_cast<int64_t>(seg_r0 + m) * a.H + col] = f32_to_bf16(acc[i][j][q]);
+                for (int q = 0; q < 4; ++q) {
+                    const int col = nt * BN + wn * (BN / 2) + j * 32 + 8 * q + 4 * khalf;
+                    if (col < a.H) {
+                        uint2 o;
+                        o.x = pack_bf16x2(acc[j][i][4 * q], acc[j][i][4 * q + 1]);
+                        o.y = pack_bf16x2(acc[j][i][4 * q + 2], acc[j][i][4 * q + 3]);
+                        *reinterpret_cast<uint2*>(crow + col) = o;
+                    }
                 }
             }
         }
@@ -459,9 +534,22 @@ __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
     }
 }
 
-// tile shapes of the bf16 path
-constexpr int G1_BM = 128, G1_BN = 128, G1_WM = 2, G1_WN = 2;
-constexpr int G2_BM = 128, G2_BN = 128, G2_WM = 2, G2_WN = 2;
+// Tile shapes of the bf16 path (workgroup BM x BN, 2 x 2 waves).  The gate/up
+// GEMM's BN counts gate and up rows together (BN/2 act columns per tile).
+#ifndef LBV_G1_BM
+#define LBV_G1_BM 256
+#endif
+#ifndef LBV_G1_BN
+#define LBV_G1_BN 256
+#endif
+#ifndef LBV_G2_BM
+#define LBV_G2_BM 256
+#endif
+#ifndef LBV_G2_BN
+#define LBV_G2_BN 256
+#endif
+constexpr int G1_BM = LBV_G1_BM, G1_BN = LBV_G1_BN;
+constexpr int G2_BM = LBV_G2_BM, G2_BN = LBV_G2_BN;
 
 GemmArgs make_args(const Dims& d) {
     GemmArgs a;
@@ -496,7 +584,7 @@ hipError_t launch_gemm_w13(const Dims& d, const void* x, const void* w13,
     if (d.bf16) {
         a.ntn = (d.I + G1_BN / 2 - 1) / (G1_BN / 2);
         const int64_t grid = max_mtiles(d, G1_BM) * a.ntn;
-        hipLaunchKernelGGL((gemm_bf16_kernel<G1_BM, G1_BN, 64, G1_WM, G1_WN, 0>),
+        hipLaunchKernelGGL((gemm_bf16_kernel<G1_BM, G1_BN, 0>),
                            dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
     } else {
         a.ntn = (d.I + 31) / 32;
@@ -521,7 +609,7 @@ hipError_t launch_gemm_w2(const Dims& d, const void* act, const void* w2, const 
     if (d.bf16) {
         a.ntn = (d.H + G2_BN - 1) / G2_BN;
         const int64_t grid = max_mtiles(d, G2_BM) * a.ntn;
-        hipLaunchKernelGGL((gemm_bf16_kernel<G2_BM, G2_BN, 64, G2_WM, G2_WN, 1>),
+        hipLaunchKernelGGL((gemm_bf16_kernel<G2_BM, G2_BN, 1>),
                            dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
     } else {
         a.ntn = (d.H + 31) / 32;
