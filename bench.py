@@ -112,11 +112,13 @@ def main():
                       device="cuda")
     act = torch.empty(T * KS, I, dtype=x.dtype, device="cuda")
     yws = torch.empty(lbv.lbv_moe_w2_workspace_size(cfg, T), dtype=torch.uint8, device="cuda")
+    rws = torch.empty(max(lbv.lbv_moe_route_workspace_size(cfg), 16), dtype=torch.uint8,
+                      device="cuda")
     stages = ["route", "permute", "gemm_w13_silu", "gemm_w2_combine"]
 
     def split(evs):
         evs[0].record(stream)
-        lbv.lbv_moe_route(cfg, x, router_w, e_bias, mask, ids, wts, stream)
+        lbv.lbv_moe_route(cfg, x, router_w, e_bias, mask, ids, wts, rws, stream)
         evs[1].record(stream)
         lbv.lbv_moe_permute(cfg, ids, off, srt, inv, pws, stream)
         evs[2].record(stream)

@@ -103,12 +103,15 @@ lbv_status lbv_moe_check_config(const lbv_moe_config *cfg);
 /*
  * Workspace sizes in bytes.
  *   lbv_moe_workspace_size:          for lbv_moe_forward;
+ *   lbv_moe_route_workspace_size:    for lbv_moe_route (does not depend on T;
+ *                                    3 E H bf16 values on the bf16 path, else 0);
  *   lbv_moe_permute_workspace_size:  for lbv_moe_permute;
  *   lbv_moe_w2_workspace_size:       for lbv_moe_gemm_w2_combine.
  * Sizes grow linearly with T (the forward one is dominated by the bf16 expert
  * output buffer, T (K + ns) H elements).
  */
 lbv_status lbv_moe_workspace_size(const lbv_moe_config *cfg, int64_t T, size_t *bytes);
+lbv_status lbv_moe_route_workspace_size(const lbv_moe_config *cfg, size_t *bytes);
 lbv_status lbv_moe_permute_workspace_size(const lbv_moe_config *cfg, int64_t T, size_t *bytes);
 lbv_status lbv_moe_w2_workspace_size(const lbv_moe_config *cfg, int64_t T, size_t *bytes);
 
@@ -123,11 +126,18 @@ lbv_status lbv_moe_w2_workspace_size(const lbv_moe_config *cfg, int64_t T, size_
  *                     descending then id ascending; -1 for padding tokens
  *   topk_w   [T, K]   fp32 out: routing weights, already scaled by
  *                     routed_scaling_factor; 0 for padding tokens
+ *   ws, ws_bytes      scratch of lbv_moe_route_workspace_size bytes (may be
+ *                     NULL when that size is 0).  With bf16 x the router
+ *                     weight is split there into three bf16 planes whose sum
+ *                     is exactly W_r, so the fp32 logits run on the bf16
+ *                     matrix cores; finite W_r entries must stay below the
+ *                     bf16 overflow threshold (about 3.39e38).
  * Ties between equal scores go to the lower group / expert index.
  */
 lbv_status lbv_moe_route(const lbv_moe_config *cfg, int64_t T, const void *x,
                          const float *router_w, const float *e_bias, const uint8_t *mask,
-                         int32_t *topk_ids, float *topk_w, hipStream_t stream);
+                         int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes,
+                         hipStream_t stream);
 
 /*
  * Token-to-expert permutation (vLLM-Omni article, "MoE 实现的源码级要点":

@@ -17,7 +17,8 @@ import torch  # noqa: F401  (loads the HIP runtime that the library binds to)
 
 __all__ = [
     "LbvError", "MoEConfig", "config", "load", "lbv_abi_version", "lbv_status_string",
-    "lbv_moe_check_config", "lbv_moe_workspace_size", "lbv_moe_permute_workspace_size",
+    "lbv_moe_check_config", "lbv_moe_workspace_size", "lbv_moe_route_workspace_size",
+    "lbv_moe_permute_workspace_size",
     "lbv_moe_w2_workspace_size", "lbv_moe_route", "lbv_moe_permute", "lbv_moe_gemm_w13_silu",
     "lbv_moe_gemm_w2_combine", "lbv_moe_forward", "EXPORTS", "LIB_PATH",
 ]
@@ -32,7 +33,7 @@ LBV_SCORE_SIGMOID, LBV_SCORE_SOFTMAX = 0, 1
 
 EXPORTS = (
     "lbv_abi_version", "lbv_status_string", "lbv_moe_check_config", "lbv_moe_workspace_size",
-    "lbv_moe_permute_workspace_size", "lbv_moe_w2_workspace_size", "lbv_moe_route",
+    "lbv_moe_route_workspace_size", "lbv_moe_permute_workspace_size", "lbv_moe_w2_workspace_size", "lbv_moe_route",
     "lbv_moe_permute", "lbv_moe_gemm_w13_silu", "lbv_moe_gemm_w2_combine", "lbv_moe_forward",
 )
 
@@ -97,7 +98,9 @@ def load():
               "lbv_moe_w2_workspace_size"):
         getattr(L, n).argtypes = [C, I64, ctypes.POINTER(SZ)]
         getattr(L, n).restype = st
-    L.lbv_moe_route.argtypes = [C, I64, P, P, P, P, P, P, P]
+    L.lbv_moe_route_workspace_size.argtypes = [C, ctypes.POINTER(SZ)]
+    L.lbv_moe_route_workspace_size.restype = st
+    L.lbv_moe_route.argtypes = [C, I64, P, P, P, P, P, P, P, SZ, P]
     L.lbv_moe_route.restype = st
     L.lbv_moe_permute.argtypes = [C, I64, P, P, P, P, P, SZ, P]
     L.lbv_moe_permute.restype = st
@@ -164,6 +167,13 @@ def lbv_moe_workspace_size(cfg: MoEConfig, T: int) -> int:
     return _size("lbv_moe_workspace_size", cfg, T)
 
 
+def lbv_moe_route_workspace_size(cfg: MoEConfig) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().lbv_moe_route_workspace_size(ctypes.byref(cfg), ctypes.byref(n)),
+           "lbv_moe_route_workspace_size")
+    return n.value
+
+
 def lbv_moe_permute_workspace_size(cfg: MoEConfig, T: int) -> int:
     return _size("lbv_moe_permute_workspace_size", cfg, T)
 
@@ -172,13 +182,14 @@ def lbv_moe_w2_workspace_size(cfg: MoEConfig, T: int) -> int:
     return _size("lbv_moe_w2_workspace_size", cfg, T)
 
 
-def lbv_moe_route(cfg, x, router_w, e_bias, mask, topk_ids, topk_w, stream=None):
+def lbv_moe_route(cfg, x, router_w, e_bias, mask, topk_ids, topk_w, ws=None, stream=None):
     dt = cfg.torch_dtype
     _check(load().lbv_moe_route(
         ctypes.byref(cfg), x.shape[0], _ptr(x, "x", dt), _ptr(router_w, "router_w", torch.float32),
         _ptr(e_bias, "e_bias", torch.float32), _ptr(mask, "mask", torch.uint8),
         _ptr(topk_ids, "topk_ids", torch.int32), _ptr(topk_w, "topk_w", torch.float32),
-        _stream(stream)), "lbv_moe_route")
+        _ptr(ws, "ws"), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
+        "lbv_moe_route")
 
 
 def lbv_moe_permute(cfg, topk_ids, offsets, sorted_rows, inv_rows, ws, stream=None):

@@ -78,7 +78,7 @@ size_t elem_bytes(const Dims& d) { return d.bf16 ? 2 : 4; }
 
 // Forward workspace layout (each part 256-byte aligned).
 struct FwdLayout {
-    size_t ids, w, offsets, sorted, inv, perm, act, y, total;
+    size_t ids, w, offsets, sorted, inv, perm, route, act, y, total;
 };
 
 FwdLayout fwd_layout(const Dims& d) {
@@ -91,6 +91,7 @@ FwdLayout fwd_layout(const Dims& d) {
     L.sorted = off;  off += round_up(T * d.KS * sizeof(int32_t));
     L.inv = off;     off += round_up(T * d.KS * sizeof(int32_t));
     L.perm = off;    off += round_up(lbv::permute_ws_bytes(d));
+    L.route = off;   off += round_up(lbv::route_ws_bytes(d));
     L.act = off;     off += round_up(T * d.KS * d.I * elem_bytes(d));
     L.y = off;       off += round_up(T * d.KS * d.H * elem_bytes(d));
     L.total = off;
@@ -139,6 +140,15 @@ lbv_status lbv_moe_workspace_size(const lbv_moe_config* cfg, int64_t T, size_t* 
     return LBV_OK;
 }
 
+lbv_status lbv_moe_route_workspace_size(const lbv_moe_config* cfg, size_t* bytes) {
+    if (!bytes) return LBV_ERR_NULL;
+    Dims d;
+    lbv_status st = make_dims(cfg, 0, &d);
+    if (st != LBV_OK) return st;
+    *bytes = round_up(lbv::route_ws_bytes(d));
+    return LBV_OK;
+}
+
 lbv_status lbv_moe_permute_workspace_size(const lbv_moe_config* cfg, int64_t T, size_t* bytes) {
     if (!bytes) return LBV_ERR_NULL;
     Dims d;
@@ -159,16 +169,20 @@ lbv_status lbv_moe_w2_workspace_size(const lbv_moe_config* cfg, int64_t T, size_
 
 lbv_status lbv_moe_route(const lbv_moe_config* cfg, int64_t T, const void* x,
                          const float* router_w, const float* e_bias, const uint8_t* mask,
-                         int32_t* topk_ids, float* topk_w, hipStream_t stream) {
+                         int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
     Dims d;
     lbv_status st = make_dims(cfg, T, &d);
     if (st != LBV_OK) return st;
     if (T == 0) return LBV_OK;
-    if (!x || !router_w || !e_bias || !topk_ids || !topk_w) return LBV_ERR_NULL;
+    const size_t need = round_up(lbv::route_ws_bytes(d));
+    if (!x || !router_w || !e_bias || !topk_ids || !topk_w || (need > 0 && !ws))
+        return LBV_ERR_NULL;
     if (!aligned16(x) || !aligned16(router_w) || !aligned4(e_bias) || !aligned4(topk_ids) ||
-        !aligned4(topk_w))
+        !aligned4(topk_w) || !aligned16(ws))
         return LBV_ERR_ALIGN;
-    return hip_status(lbv::launch_route(d, x, router_w, e_bias, mask, topk_ids, topk_w, stream));
+    if (ws_bytes < need) return LBV_ERR_WORKSPACE;
+    return hip_status(lbv::launch_route(d, x, router_w, e_bias, mask, topk_ids, topk_w, ws, stream));
 }
 
 lbv_status lbv_moe_permute(const lbv_moe_config* cfg, int64_t T, const int32_t* topk_ids,
@@ -251,10 +265,11 @@ lbv_status lbv_moe_forward(const lbv_moe_config* cfg, int64_t T, const void* x,
     int32_t* sorted = reinterpret_cast<int32_t*>(base + L.sorted);
     int32_t* inv = reinterpret_cast<int32_t*>(base + L.inv);
     void* perm = base + L.perm;
+    void* rws = base + L.route;
     void* act = base + L.act;
     void* y = base + L.y;
 
-    hipError_t e = lbv::launch_route(d, x, router_w, e_bias, mask, ids, w, stream);
+    hipError_t e = lbv::launch_route(d, x, router_w, e_bias, mask, ids, w, rws, stream);
     if (e == hipSuccess) e = lbv::launch_permute(d, ids, offsets, sorted, inv, perm, stream);
     if (e == hipSuccess) e = lbv::launch_gemm_w13(d, x, w13, shared_w13, offsets, sorted, act, stream);
     if (e == hipSuccess) e = lbv::launch_gemm_w2(d, act, w2, shared_w2, offsets, y, stream);

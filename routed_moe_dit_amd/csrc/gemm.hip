@@ -29,6 +29,32 @@
 #include <type_traits>
 
 #include "lbv_internal.h"
+#include "lbv_pipe.h"
+
+// Compile-time shape of the bf16 path: workgroup tile BM x BN (2 x 2 waves;
+// the gate/up GEMM's BN counts gate and up rows together, BN/2 act columns
+// per tile), and the k-depth BK and number STAGES of the LDS ring.
+#ifndef LBV_BK
+#define LBV_BK 32
+#endif
+#ifndef LBV_STAGES
+#define LBV_STAGES 4
+#endif
+#ifndef LBV_KK_UNROLL
+#define LBV_KK_UNROLL 2
+#endif
+#ifndef LBV_G1_BM
+#define LBV_G1_BM 256
+#endif
+#ifndef LBV_G1_BN
+#define LBV_G1_BN 256
+#endif
+#ifndef LBV_G2_BM
+#define LBV_G2_BM 256
+#endif
+#ifndef LBV_G2_BN
+#define LBV_G2_BN 256
+#endif
 
 namespace lbv {
 namespace {
@@ -96,61 +122,30 @@ __device__ bool find_tile(const GemmArgs& a, int BM, int mt, int* seg_out, int* 
     return true;
 }
 
-// Waits until at most N vector-memory operations of this wave are in flight.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+// 16-byte chunk swizzle of an LDS row of BK bf16: chunk c of row r is stored at
+// c ^ swz<BK>(r).  Chosen by measurement on gfx950 for the MFMA fragment read
+// (lanes 0-31 read rows r0 + lane, lanes 32-63 the next chunk), whose
+// ds_read_b128 then runs at ~210 B/clk/CU (conflict-free):
+//   64-byte rows:  c ^ ((r >> 2) & 3)   (unswizzled: ~62, c ^ ((r>>1)&3): ~120)
+//   128-byte rows: c ^ ((r >> 1) & 7)   (c ^ (r & 7): ~120)
+template <int BK>
+__device__ __forceinline__ int swz(int r) {
+    static_assert(BK == 32 || BK == 64, "row of 64 or 128 bytes");
+    return BK == 32 ? ((r >> 2) & 3) : ((r >> 1) & 7);
 }
 
-// Workgroup barrier without the memory fence that __syncthreads() implies (the
-// fence would wait for every load in flight, i.e. drain the prefetch queue).
-// The empty asm keeps the compiler from moving memory accesses across it.
-__device__ __forceinline__ void block_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// Asynchronous 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4):
-// lane l's 16 bytes land at LDS byte address lds_base + 16 l.  Written as asm
-// so that the compiler's wait-count pass, which cannot tell the stage being
-// filled from the stage being read, does not drain the queue before every LDS
-// read; the kernel orders these copies itself (wait_vmcnt + block_barrier).
-// The instruction has no register results.
-__device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t lds_base) {
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off"
-        :
-        : "s"(lds_base), "v"(gsrc)
-        : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)p));
-}
-
-// 16-byte chunk swizzle of a 64-byte LDS row (4 chunks): chunk c of row r is
-// stored at c ^ ((r >> 2) & 3).  Measured on gfx950 for the fragment read
-// (lanes 0-31 rows r0 + lane, lanes 32-63 the next chunk): ~209 B/clk/CU, i.e.
-// conflict-free, against ~62 B/clk unswizzled and ~120 B/clk for
-// c ^ ((r >> 1) & 3).
-__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
-
-template <int BM, int BN, int MODE>
+template <int BM, int BN, int BK, int STAGES, int MODE>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
-    constexpr int BK = 32;                       // bf16 per row per stage (64 bytes)
-    constexpr int STAGES = 4;                    // LDS ring: STAGES-1 k-tiles in flight
+    // BK: bf16 per row per stage (64 or 128 bytes); STAGES: LDS ring of
+    // k-tiles, STAGES - 1 of them in flight while one is multiplied.
+    static_assert(STAGES == 2 || STAGES == 4, "2 or 4 stages");
     constexpr int TM = BM / 64;                  // token tiles (32 rows) per wave
     constexpr int TN = BN / 64;                  // weight-row tiles (32 rows) per wave
     static_assert(MODE == 1 || TN % 2 == 0, "gate/up tiles come in pairs");
     constexpr int STAGE = (BM + BN) * BK;        // bf16 elements per stage
-    constexpr int AI = BM / 64, BI = BN / 64;    // 1 KB load instructions per wave per stage
+    constexpr int CPR = BK / 8;                  // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;                // rows per 1 KB copy instruction
+    constexpr int AI = BM / 4 / RPI, BI = BN / 4 / RPI;  // copies per wave per stage
     constexpr int NI = AI + BI;
 
     // Four distinct LDS objects (not one array indexed by kt % 4): with the
@@ -159,8 +154,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     // drain the whole load queue before every LDS read.
     __shared__ __attribute__((aligned(1024))) uint16_t lds0[STAGE];
     __shared__ __attribute__((aligned(1024))) uint16_t lds1[STAGE];
-    __shared__ __attribute__((aligned(1024))) uint16_t lds2[STAGE];
-    __shared__ __attribute__((aligned(1024))) uint16_t lds3[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds2[STAGES > 2 ? STAGE : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds3[STAGES > 3 ? STAGE : 8];
     __shared__ int s_tmp[8];
     __shared__ int s_sel[2];
 
@@ -178,16 +173,16 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     const int jsh = seg - a.E;
     const int Is = a.NS * a.I;
 
-    // ---- global source of each lane's 16-byte chunk (per load instruction) ----
-    // Instruction i of wave w fills LDS rows w*(rows/4) + 16 i + [0, 16) of the
-    // stage; lane l lands at row +l/4, physical chunk l%4, which holds logical
-    // chunk (l%4) ^ swz(row).
+    // ---- global source of each lane's 16-byte chunk (per copy instruction) ----
+    // Instruction i of wave w fills LDS rows w*(rows/4) + RPI i + [0, RPI) of
+    // the stage; lane l lands at row +l/CPR, physical chunk l%CPR, which holds
+    // logical chunk (l%CPR) ^ swz(row).
     const uint16_t* aptr[AI];
     const uint16_t* bptr[BI];
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
-        const int r = wave * (BM / 4) + i * 16 + (lane >> 2);
-        const int c = (lane & 3) ^ swz(r);
+        const int r = wave * (BM / 4) + i * RPI + lane / CPR;
+        const int c = (lane % CPR) ^ swz<BK>(r);
         int m = m0 + r;
         if (m >= seg_n) m = seg_n - 1;
         if (MODE == 0) {
@@ -201,8 +196,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < BI; ++i) {
-        const int r = wave * (BN / 4) + i * 16 + (lane >> 2);
-        const int c = (lane & 3) ^ swz(r);
+        const int r = wave * (BN / 4) + i * RPI + lane / CPR;
+        const int c = (lane % CPR) ^ swz<BK>(r);
         if (MODE == 0) {
             const int half = r / (BN / 2);
             int n = nt * (BN / 2) + (r % (BN / 2));
@@ -229,22 +224,26 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     const int a_lds = wave * (BM / 4) * BK;          // element offsets inside a stage
     const int b_lds = BM * BK + wave * (BN / 4) * BK;
 
+    const int nk = a.kdim / BK;
+
     auto stage_buf = [&](auto S) -> uint16_t* {
+        static_assert(decltype(S)::value < STAGES, "stage index");
         if constexpr (decltype(S)::value == 0) return lds0;
         else if constexpr (decltype(S)::value == 1) return lds1;
         else if constexpr (decltype(S)::value == 2) return lds2;
         else return lds3;
     };
-    auto issue = [&](auto S, int kt) {     // k-tile kt into stage S
+    // k-tile kt into stage S: NI copy instructions per wave
+    auto issue = [&](auto S, int kt) {
         const int k0 = kt * BK;
         uint16_t* st = stage_buf(S);
         const uint32_t base = lds_addr(st);
 #pragma unroll
         for (int i = 0; i < AI; ++i)
-            lds_dma16(aptr[i] + k0, base + (a_lds + i * 16 * BK) * 2);
+            lds_dma16(aptr[i] + k0, base + (a_lds + i * RPI * BK) * 2);
 #pragma unroll
         for (int i = 0; i < BI; ++i)
-            lds_dma16(bptr[i] + k0, base + (b_lds + i * 16 * BK) * 2);
+            lds_dma16(bptr[i] + k0, base + (b_lds + i * RPI * BK) * 2);
     };
 
     // ---- fragments: weight rows are the MFMA's first operand, token rows the
@@ -272,37 +271,50 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[j][i][q] = 0.f;
 
-    const int nk = a.kdim / BK;
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
     using S2 = std::integral_constant<int, 2>;
     using S3 = std::integral_constant<int, 3>;
     issue(S0{}, 0);
-    if (1 < nk) issue(S1{}, 1);
-    if (2 < nk) issue(S2{}, 2);
+    if constexpr (STAGES > 2) {
+        if (1 < nk) issue(S1{}, 1);
+    }
+    if constexpr (STAGES > 3) {
+        if (2 < nk) issue(S2{}, 2);
+    }
 
     // one k-tile: wait for its stage, free the previous stage, refill it with
     // k-tile kt + 3, multiply
     auto step = [&](auto S, int kt) {
         constexpr int SI = decltype(S)::value;
-        const int ahead = nk - 1 - kt;            // k-tiles issued after kt
-        if (ahead >= STAGES - 2) wait_vmcnt<(STAGES - 2) * NI>();
-        else if (ahead == 1) wait_vmcnt<NI>();
-        else wait_vmcnt<0>();
+        // copies of k-tile kt done; still in flight: the k-tiles issued after
+        // it (at most STAGES - 2 of them)
+        const int ahead = nk - 1 - kt;
+        if constexpr (STAGES > 3) {
+            if (ahead >= 2) wait_vmcnt<2 * NI>();
+            else if (ahead == 1) wait_vmcnt<NI>();
+            else wait_vmcnt<0>();
+        } else if constexpr (STAGES > 2) {
+            if (ahead >= 1) wait_vmcnt<NI>();
+            else wait_vmcnt<0>();
+        } else {
+            wait_vmcnt<0>();
+        }
         block_barrier();
-        if (kt + STAGES - 1 < nk) issue(std::integral_constant<int, (SI + 3) % 4>{}, kt + STAGES - 1);
+        if (kt + STAGES - 1 < nk)
+            issue(std::integral_constant<int, (SI + STAGES - 1) % STAGES>{}, kt + STAGES - 1);
         const uint16_t* As = stage_buf(S);
         const uint16_t* Bs = As + BM * BK;
-#pragma unroll
+#pragma unroll LBV_KK_UNROLL
         for (int kk = 0; kk < BK / 16; ++kk) {
             const int ch = kk * 2 + khalf;
             bf16x8 tf[TM], wf[TN];
 #pragma unroll
             for (int i = 0; i < TM; ++i)
-                tf[i] = *reinterpret_cast<const bf16x8*>(As + trow[i] * BK + ((ch ^ swz(trow[i])) * 8));
+                tf[i] = *reinterpret_cast<const bf16x8*>(As + trow[i] * BK + ((ch ^ swz<BK>(trow[i])) * 8));
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                wf[j] = *reinterpret_cast<const bf16x8*>(Bs + wrow[j] * BK + ((ch ^ swz(wrow[j])) * 8));
+                wf[j] = *reinterpret_cast<const bf16x8*>(Bs + wrow[j] * BK + ((ch ^ swz<BK>(wrow[j])) * 8));
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -310,63 +322,77 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
                     acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], tf[i], acc[j][i], 0, 0, 0);
         }
     };
-    for (int kt = 0; kt < nk; kt += 4) {
+    for (int kt = 0; kt < nk; kt += STAGES) {
         step(S0{}, kt);
         if (kt + 1 < nk) step(S1{}, kt + 1);
-        if (kt + 2 < nk) step(S2{}, kt + 2);
-        if (kt + 3 < nk) step(S3{}, kt + 3);
+        if constexpr (STAGES > 2) {
+            if (kt + 2 < nk) step(S2{}, kt + 2);
+        }
+        if constexpr (STAGES > 3) {
+            if (kt + 3 < nk) step(S3{}, kt + 3);
+        }
     }
 
-    // ---- epilogue: lane holds columns 8q + 4*khalf + [0,4) of row (lane & 31) ----
-    uint16_t* C = static_cast<uint16_t*>(a.C);
-    if (MODE == 0) {
-        constexpr int HT = TN / 2;
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int m = m0 + wm * (BM / 2) + i * 32 + (lane & 31);
-            if (m >= seg_n) continue;
-            uint16_t* crow = C + static_cast<int64_t>(seg_r0 + m) * a.I;
-#pragma unroll
-            for (int j = 0; j < HT; ++j) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int col = nt * (BN / 2) + wn * (BN / 4) + j * 32 + 8 * q + 4 * khalf;
-                    float v[4];
-#pragma unroll
-                    for (int p = 0; p < 4; ++p) {
-                        const float g = acc[j][i][4 * q + p];
-                        const float u = acc[j + HT][i][4 * q + p];
-                        v[p] = g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-                    }
-                    if (col < a.I) {
-                        uint2 o;
-                        o.x = pack_bf16x2(v[0], v[1]);
-                        o.y = pack_bf16x2(v[2], v[3]);
-                        *reinterpret_cast<uint2*>(crow + col) = o;
-                    }
-                }
-            }
-        }
+    // ---- epilogue ---------------------------------------------------------------
+    // Lane holds, for token tile i and weight tile j, output columns
+    // 8q + 4*khalf + [0, 4) of token row (lane & 31).  Each wave first writes
+    // its tile as bf16 into its own LDS region (row pitch = its column count,
+    // 16-byte chunks XOR-swizzled by row), then reads it back 16 bytes per lane
+    // so that every global store instruction writes whole contiguous rows.
+    constexpr int WCOLS = MODE == 0 ? BN / 4 : BN / 2;   // output columns per wave
+    constexpr int CHUNKS = WCOLS / 8;                    // 16-byte chunks per row
+    block_barrier();                                     // all waves done with the stages
+    uint16_t* ep;                                        // this wave's region (128 x WCOLS)
+    if constexpr (STAGES == 4) {
+        static_assert(128 * WCOLS <= STAGE, "one wave tile per stage buffer");
+        ep = wave == 0 ? lds0 : wave == 1 ? lds1 : wave == 2 ? lds2 : lds3;
     } else {
+        static_assert(STAGES == 2 && 2 * 128 * WCOLS <= STAGE, "two wave tiles per stage buffer");
+        ep = ((wave & 1) ? lds1 : lds0) + (wave >> 1) * 128 * WCOLS;
+    }
+    auto ep_off = [&](int row, int col) {                // element offset of (row, col) in the region
+        return row * WCOLS + (((col >> 3) ^ (row % CHUNKS)) << 3) + (col & 7);
+    };
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int m = m0 + wm * (BM / 2) + i * 32 + (lane & 31);
-            if (m >= seg_n) continue;
-            uint16_t* crow = C + static_cast<int64_t>(seg_r0 + m) * a.H;
+    for (int i = 0; i < TM; ++i) {
+        const int row = i * 32 + (lane & 31);
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
+        for (int j = 0; j < (MODE == 0 ? TN / 2 : TN); ++j) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int col = nt * BN + wn * (BN / 2) + j * 32 + 8 * q + 4 * khalf;
-                    if (col < a.H) {
-                        uint2 o;
-                        o.x = pack_bf16x2(acc[j][i][4 * q], acc[j][i][4 * q + 1]);
-                        o.y = pack_bf16x2(acc[j][i][4 * q + 2], acc[j][i][4 * q + 3]);
-                        *reinterpret_cast<uint2*>(crow + col) = o;
+            for (int q = 0; q < 4; ++q) {
+                const int col = j * 32 + 8 * q + 4 * khalf;
+                float v[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    if (MODE == 0) {
+                        const float g = acc[j][i][4 * q + p];
+                        const float u = acc[j + TN / 2][i][4 * q + p];
+                        v[p] = g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+                    } else {
+                        v[p] = acc[j][i][4 * q + p];
                     }
                 }
+                uint2 o;
+                o.x = pack_bf16x2(v[0], v[1]);
+                o.y = pack_bf16x2(v[2], v[3]);
+                *reinterpret_cast<uint2*>(ep + ep_off(row, col)) = o;
             }
         }
+    }
+    // read back: lane -> (row, chunk); a pass covers 64 / CHUNKS rows
+    const int ncols = MODE == 0 ? a.I : a.H;
+    const int col0 = MODE == 0 ? nt * (BN / 2) + wn * (BN / 4) : nt * BN + wn * (BN / 2);
+    uint16_t* C = static_cast<uint16_t*>(a.C);
+    constexpr int RPP = 64 / CHUNKS;                     // rows per pass
+#pragma unroll 4
+    for (int r0 = 0; r0 < 128; r0 += RPP) {
+        const int row = r0 + lane / CHUNKS;
+        const int ch = lane % CHUNKS;
+        const int m = m0 + wm * (BM / 2) + row;
+        const int col = col0 + ch * 8;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(ep + ep_off(row, ch * 8));
+        if (m < seg_n && col < ncols)
+            *reinterpret_cast<u32x4*>(C + static_cast<int64_t>(seg_r0 + m) * ncols + col) = v;
     }
 }
 
@@ -534,20 +560,6 @@ __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
     }
 }
 
-// Tile shapes of the bf16 path (workgroup BM x BN, 2 x 2 waves).  The gate/up
-// GEMM's BN counts gate and up rows together (BN/2 act columns per tile).
-#ifndef LBV_G1_BM
-#define LBV_G1_BM 256
-#endif
-#ifndef LBV_G1_BN
-#define LBV_G1_BN 256
-#endif
-#ifndef LBV_G2_BM
-#define LBV_G2_BM 256
-#endif
-#ifndef LBV_G2_BN
-#define LBV_G2_BN 256
-#endif
 constexpr int G1_BM = LBV_G1_BM, G1_BN = LBV_G1_BN;
 constexpr int G2_BM = LBV_G2_BM, G2_BN = LBV_G2_BN;
 
@@ -584,7 +596,7 @@ hipError_t launch_gemm_w13(const Dims& d, const void* x, const void* w13,
     if (d.bf16) {
         a.ntn = (d.I + G1_BN / 2 - 1) / (G1_BN / 2);
         const int64_t grid = max_mtiles(d, G1_BM) * a.ntn;
-        hipLaunchKernelGGL((gemm_bf16_kernel<G1_BM, G1_BN, 0>),
+        hipLaunchKernelGGL((gemm_bf16_kernel<G1_BM, G1_BN, LBV_BK, LBV_STAGES, 0>),
                            dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
     } else {
         a.ntn = (d.I + 31) / 32;
@@ -609,7 +621,7 @@ hipError_t launch_gemm_w2(const Dims& d, const void* act, const void* w2, const 
     if (d.bf16) {
         a.ntn = (d.H + G2_BN - 1) / G2_BN;
         const int64_t grid = max_mtiles(d, G2_BM) * a.ntn;
-        hipLaunchKernelGGL((gemm_bf16_kernel<G2_BM, G2_BN, 1>),
+        hipLaunchKernelGGL((gemm_bf16_kernel<G2_BM, G2_BN, LBV_BK, LBV_STAGES, 1>),
                            dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
     } else {
         a.ntn = (d.H + 31) / 32;

@@ -31,8 +31,9 @@ struct Dims {
 };
 
 // Launchers (all enqueue on `stream`, return hipGetLastError()).
+size_t route_ws_bytes(const Dims& d);
 hipError_t launch_route(const Dims& d, const void* x, const float* router_w, const float* e_bias,
-                        const uint8_t* mask, int32_t* topk_ids, float* topk_w,
+                        const uint8_t* mask, int32_t* topk_ids, float* topk_w, void* ws,
                         hipStream_t stream);
 
 size_t permute_ws_bytes(const Dims& d);

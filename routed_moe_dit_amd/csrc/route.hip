@@ -23,6 +23,7 @@
 //    (order-preserving score bits, inverted index), so ties go to the lower
 //    index exactly as in a sequential scan.
 #include "lbv_internal.h"
+#include "lbv_pipe.h"
 
 namespace lbv {
 namespace {
@@ -277,11 +278,311 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     }
 }
 
+// ===========================================================================
+// bf16 path (x stored as bf16, E <= 128, n_group <= 8, G % 4 == 0, K <= 16)
+// ===========================================================================
+//
+// Logits on the bf16 matrix cores, exactly in fp32 terms: the fp32 router
+// weight is split once per call into three bf16 planes with
+// W = hi + mid + lo exactly (hi = RNE(W), mid = RNE(W - hi), lo = W - hi - mid,
+// which fits bf16 for every finite W below the bf16 overflow threshold).  x is
+// bf16, so each product x*plane is exact in fp32 and the MFMA sums them in
+// fp32: the logit is an fp32 dot product, in a different summation order.
+//
+// One workgroup routes 128 tokens.  Per 32-wide hidden slice a stage holds the
+// 128 x rows and the 3 x EP plane rows (64 bytes each), filled by
+// asynchronous copies three slices ahead.  Wave w owns expert tile w (32
+// experts) against all 4 token tiles: 3 planes x 4 = 12 MFMAs per 16-deep
+// step.  The epilogue turns logits into scores s = sigmoid(z) and selection
+// values c = s + bias in LDS; then each lane routes one token by scanning
+// its row: in-group top-2 sums, kept groups, and a sorted top-K insertion in
+// (c descending, id ascending) order over the kept groups' experts.
+
+constexpr int RV_TOK = 128;
+constexpr int RV_BK = 32;
+constexpr int RV_STAGES = 4;
+constexpr int RV_NGMAX = 8;
+
+struct RouteV2Args {
+    const uint16_t* x;       // [T, H] bf16
+    const uint16_t* planes;  // [3, E, H] bf16
+    const float* bias;
+    const uint8_t* mask;
+    int32_t* ids;
+    float* w;
+    int64_t T;
+    int H, E, K, NG, TG, G, norm;
+    float rsf;
+};
+
+__global__ __launch_bounds__(256) void router_split_kernel(const float* wr, uint16_t* planes,
+                                                           int64_t n) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= n) return;
+    const float w = wr[i];
+    const uint16_t hi = f32_to_bf16(w);
+    const float r1 = w - bf16_to_f32(hi);
+    const uint16_t mid = f32_to_bf16(r1);
+    const float r2 = r1 - bf16_to_f32(mid);
+    planes[i] = hi;
+    planes[n + i] = mid;
+    planes[2 * n + i] = f32_to_bf16(r2);
+}
+
+__device__ __forceinline__ int rswz(int r) { return (r >> 2) & 3; }   // 64-byte rows
+
+template <int EP, int KMAX>
+__global__ __launch_bounds__(256) void route_bf16_kernel(RouteV2Args a) {
+    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+    typedef float f32x16 __attribute__((ext_vector_type(16)));
+    constexpr int ROWS = RV_TOK + 3 * EP;                 // stage rows
+    constexpr int STAGE = ROWS * RV_BK;                   // bf16 elements
+    constexpr int NI = ROWS / 64;                         // copies per wave per stage (16 rows each)
+    static_assert(ROWS % 64 == 0, "stage rows split over 4 waves");
+    constexpr int PITCH = EP + 4;                         // floats per token row of c / s
+    constexpr int STAGE_BYTES = RV_STAGES * STAGE * 2;
+    constexpr int CS_BYTES = 2 * RV_TOK * PITCH * 4;
+    constexpr int SMEM = STAGE_BYTES > CS_BYTES ? STAGE_BYTES : CS_BYTES;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[SMEM / 2];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * RV_TOK;
+    const int H = a.H, E = a.E;
+
+    // ---- copy sources: instruction i of this wave fills stage rows
+    // wave * (ROWS/4) + 16 i + lane/4, logical chunk (lane%4) ^ rswz(row) ----
+    const uint16_t* src[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int r = wave * (ROWS / 4) + i * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ rswz(r);
+        if (r < RV_TOK) {
+            int64_t t = t0 + r;
+            if (t >= a.T) t = a.T - 1;
+            src[i] = a.x + t * H + c * 8;
+        } else {
+            const int q = r - RV_TOK;
+            const int p = q / EP;
+            int e = q % EP;
+            if (e >= E) e = E - 1;
+            src[i] = a.planes + (static_cast<int64_t>(p) * E + e) * H + c * 8;
+        }
+    }
+    auto issue = [&](int kt) {
+        const uint32_t base = lds_addr(smem + (kt % RV_STAGES) * STAGE);
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            lds_dma16(src[i] + kt * RV_BK, base + (wave * (ROWS / 4) + i * 16) * RV_BK * 2);
+    };
+
+    const int khalf = lane >> 5;
+    const bool has_tile = wave * 32 < EP;                 // EP = 64: waves 2, 3 idle in the MFMA
+    f32x16 acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][q] = 0.f;
+
+    const int nk = H / RV_BK;
+    issue(0);
+    if (1 < nk) issue(1);
+    if (2 < nk) issue(2);
+    for (int kt = 0; kt < nk; ++kt) {
+        const int ahead = nk - 1 - kt;
+        if (ahead >= 2) wait_vmcnt<2 * NI>();
+        else if (ahead == 1) wait_vmcnt<NI>();
+        else wait_vmcnt<0>();
+        block_barrier();
+        if (kt + 3 < nk) issue(kt + 3);
+        if (has_tile) {
+            const uint16_t* st = smem + (kt % RV_STAGES) * STAGE;
+#pragma unroll
+            for (int kk = 0; kk < RV_BK / 16; ++kk) {
+                const int ch = kk * 2 + khalf;
+                bf16x8 tf[4], wf[3];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = i * 32 + (lane & 31);
+                    tf[i] = *reinterpret_cast<const bf16x8*>(st + r * RV_BK + ((ch ^ rswz(r)) * 8));
+                }
+#pragma unroll
+                for (int p = 0; p < 3; ++p) {
+                    const int r = RV_TOK + p * EP + wave * 32 + (lane & 31);
+                    wf[p] = *reinterpret_cast<const bf16x8*>(st + r * RV_BK + ((ch ^ rswz(r)) * 8));
+                }
+#pragma unroll
+                for (int p = 0; p < 3; ++p)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[p], tf[i], acc[i], 0, 0, 0);
+            }
+        }
+    }
+
+    // ---- scores to LDS: lane holds experts 8q + 4*khalf + [0,4) of token (lane&31) ----
+    block_barrier();
+    float* Cs = reinterpret_cast<float*>(smem);
+    float* Ss = Cs + RV_TOK * PITCH;
+    if (has_tile) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tok = i * 32 + (lane & 31);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int e0 = wave * 32 + 8 * q + 4 * khalf;
+                float cv[4], sv[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const int e = e0 + p;
+                    const float z = acc[i][4 * q + p];
+                    sv[p] = 1.0f / (1.0f + expf(-z));
+                    cv[p] = e < E ? sv[p] + a.bias[e] : -INFINITY;
+                }
+                *reinterpret_cast<float4*>(Cs + tok * PITCH + e0) = make_float4(cv[0], cv[1], cv[2], cv[3]);
+                *reinterpret_cast<float4*>(Ss + tok * PITCH + e0) = make_float4(sv[0], sv[1], sv[2], sv[3]);
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- selection: lane-per-token (lanes 0-31 of every wave) -------------------
+    if (lane >= 32) return;
+    const int tok = wave * 32 + lane;
+    const int64_t t = t0 + tok;
+    if (t >= a.T) return;
+    const float* crow = Cs + tok * PITCH;
+    const int G = a.G, NG = a.NG;
+
+    // in-group top-2 sums
+    float gsc[RV_NGMAX];
+#pragma unroll
+    for (int j = 0; j < RV_NGMAX; ++j) {
+        gsc[j] = -INFINITY;
+        if (j < NG) {
+            float b1 = -INFINITY, b2 = -INFINITY;
+            for (int e = j * G; e < (j + 1) * G; e += 4) {
+                const float4 v4 = *reinterpret_cast<const float4*>(crow + e);
+                const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float v = vv[u];
+                    if (v > b1) { b2 = b1; b1 = v; }
+                    else if (v > b2) { b2 = v; }
+                }
+            }
+            gsc[j] = b1 + b2;
+        }
+    }
+    // kept groups: repeated arg-max, lower index on ties; then their indices ascending
+    uint32_t kept = 0;
+    for (int r = 0; r < a.TG; ++r) {
+        float bv = -INFINITY;
+        int bj = -1;
+#pragma unroll
+        for (int j = 0; j < RV_NGMAX; ++j)
+            if (j < NG && !((kept >> j) & 1u) && (bj < 0 || gsc[j] > bv)) { bv = gsc[j]; bj = j; }
+        kept |= 1u << bj;
+    }
+    // top-K (first KMAX) over the kept groups' experts in ascending id order
+    float v[KMAX];
+    int id[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) { v[k] = -INFINITY; id[k] = -1; }
+    uint32_t rem = kept;
+    for (int r = 0; r < a.TG; ++r) {
+        const int j = __builtin_ctz(rem);
+        rem &= rem - 1;
+        for (int e = j * G; e < (j + 1) * G; e += 4) {
+            const float4 v4 = *reinterpret_cast<const float4*>(crow + e);
+            const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float c = vv[u];
+                const int ec = e + u;
+#pragma unroll
+                for (int k = KMAX - 1; k > 0; --k) {
+                    const bool gp = c > v[k - 1];
+                    const bool gk = c > v[k];
+                    const float nv = gp ? v[k - 1] : (gk ? c : v[k]);
+                    const int ni = gp ? id[k - 1] : (gk ? ec : id[k]);
+                    v[k] = nv;
+                    id[k] = ni;
+                }
+                if (c > v[0]) { v[0] = c; id[0] = ec; }
+            }
+        }
+    }
+    // weights from the raw scores, slot order sum, scaled once
+    const float* srow = Ss + tok * PITCH;
+    const bool valid = a.mask == nullptr || a.mask[t] != 0;
+    float sk[KMAX];
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        sk[k] = 0.f;
+        if (k < a.K) {
+            sk[k] = srow[id[k]];
+            sum += sk[k];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        if (k < a.K) {
+            float wv = a.norm ? sk[k] / sum : sk[k];
+            wv = wv * a.rsf;
+            a.ids[t * a.K + k] = valid ? id[k] : -1;
+            a.w[t * a.K + k] = valid ? wv : 0.f;
+        }
+    }
+}
+
 }  // namespace
 
+bool route_bf16_path(const Dims& d) {
+    return d.bf16 && d.E <= 128 && d.NG <= RV_NGMAX && d.G % 4 == 0;
+}
+
+size_t route_ws_bytes(const Dims& d) {
+    return route_bf16_path(d) ? static_cast<size_t>(3) * d.E * d.H * sizeof(uint16_t) : 0;
+}
+
 hipError_t launch_route(const Dims& d, const void* x, const float* router_w, const float* e_bias,
-                        const uint8_t* mask, int32_t* topk_ids, float* topk_w,
+                        const uint8_t* mask, int32_t* topk_ids, float* topk_w, void* ws,
                         hipStream_t stream) {
+    if (route_bf16_path(d)) {
+        uint16_t* planes = static_cast<uint16_t*>(ws);
+        const int64_t n = static_cast<int64_t>(d.E) * d.H;
+        hipLaunchKernelGGL(router_split_kernel, dim3(static_cast<unsigned>((n + 255) / 256)),
+                           dim3(256), 0, stream, router_w, planes, n);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        RouteV2Args a;
+        a.x = static_cast<const uint16_t*>(x);
+        a.planes = planes;
+        a.bias = e_bias;
+        a.mask = mask;
+        a.ids = topk_ids;
+        a.w = topk_w;
+        a.T = d.T;
+        a.H = d.H;
+        a.E = d.E;
+        a.K = d.K;
+        a.NG = d.NG;
+        a.TG = d.TG;
+        a.G = d.G;
+        a.norm = d.norm;
+        a.rsf = d.rsf;
+        const dim3 grid(static_cast<unsigned>((d.T + RV_TOK - 1) / RV_TOK));
+        if (d.E <= 64) {
+            if (d.K <= 8) hipLaunchKernelGGL((route_bf16_kernel<64, 8>), grid, dim3(256), 0, stream, a);
+            else hipLaunchKernelGGL((route_bf16_kernel<64, 16>), grid, dim3(256), 0, stream, a);
+        } else {
+            if (d.K <= 8) hipLaunchKernelGGL((route_bf16_kernel<128, 8>), grid, dim3(256), 0, stream, a);
+            else hipLaunchKernelGGL((route_bf16_kernel<128, 16>), grid, dim3(256), 0, stream, a);
+        }
+        return hipGetLastError();
+    }
     RouteArgs a;
     a.x = x;
     a.wr = router_w;

@@ -21,7 +21,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     assert set(names) == set(lbv.EXPORTS)
     L = ctypes.CDLL(lbv.LIB_PATH)
     for n in names:
@@ -103,13 +103,22 @@ BIG = 1 << 40
 def test_route_validation_paths():
     c = lbv.config()
     L = raw()
-    r = lambda T, x, wr, b, ids, w: L.lbv_moe_route(ctypes.byref(c), T, x, wr, b, None, ids, w, None)
+    need = lbv.lbv_moe_route_workspace_size(c)
+    assert need == 3 * 128 * 2048 * 2                    # three bf16 planes of W_r
+
+    def r(T, x, wr, b, ids, w, ws=Cc, nbytes=need):
+        return L.lbv_moe_route(ctypes.byref(c), T, x, wr, b, None, ids, w, ws, nbytes, None)
+
     assert r(4, None, A, B, Cc, Cc) == lbv.LBV_ERR_NULL
+    assert r(4, A, A, B, Cc, Cc, ws=None) == lbv.LBV_ERR_NULL
     assert r(4, A + 2, A, B, Cc, Cc) == lbv.LBV_ERR_ALIGN
     assert r(4, A, A + 4, B, Cc, Cc) == lbv.LBV_ERR_ALIGN
+    assert r(4, A, A, B, Cc, Cc, nbytes=need - 1) == lbv.LBV_ERR_WORKSPACE
     assert r(-1, A, A, B, Cc, Cc) == lbv.LBV_ERR_SHAPE
     assert r(0, A, A, B, Cc, Cc) == lbv.LBV_OK                # T == 0 is a no-op
-    assert L.lbv_moe_route(None, 4, A, A, B, None, Cc, Cc, None) == lbv.LBV_ERR_NULL
+    assert L.lbv_moe_route(None, 4, A, A, B, None, Cc, Cc, Cc, need, None) == lbv.LBV_ERR_NULL
+    # the fp32 path needs no scratch
+    assert lbv.lbv_moe_route_workspace_size(lbv.config(dtype="f32")) == 0
 
 
 def test_forward_validation_paths():

@@ -55,7 +55,9 @@ def run_route(wl, d):
     T = d["x"].shape[0]
     ids = torch.empty(T, wl.top_k, dtype=torch.int32, device="cuda")
     w = torch.empty(T, wl.top_k, dtype=torch.float32, device="cuda")
-    lbv.lbv_moe_route(cfg, d["x"], d["router_w"], d["e_bias"], d["mask"], ids, w)
+    rws = torch.empty(max(lbv.lbv_moe_route_workspace_size(cfg), 16), dtype=torch.uint8,
+                      device="cuda")
+    lbv.lbv_moe_route(cfg, d["x"], d["router_w"], d["e_bias"], d["mask"], ids, w, rws)
     torch.cuda.synchronize()
     return ids.cpu().numpy(), w.cpu().numpy()
 
@@ -294,7 +296,8 @@ def test_determinism_and_split_calls():
     T, K, KS, S = wl.T, wl.top_k, wl.top_k + wl.n_shared, wl.num_experts + wl.n_shared
     ids = torch.empty(T, K, dtype=torch.int32, device="cuda")
     w = torch.empty(T, K, dtype=torch.float32, device="cuda")
-    lbv.lbv_moe_route(cfg, d["x"], d["router_w"], d["e_bias"], None, ids, w)
+    rws = torch.empty(lbv.lbv_moe_route_workspace_size(cfg), dtype=torch.uint8, device="cuda")
+    lbv.lbv_moe_route(cfg, d["x"], d["router_w"], d["e_bias"], None, ids, w, rws)
     off = torch.empty(S + 1, dtype=torch.int32, device="cuda")
     srt = torch.empty(T * KS, dtype=torch.int32, device="cuda")
     inv = torch.empty(T * KS, dtype=torch.int32, device="cuda")
