@@ -27,7 +27,9 @@
  *    synchronisation.  T == 0 is a successful no-op once the configuration
  *    is valid (no pointer is looked at, nothing is enqueued).
  *  - Layout: row-major, densely packed.  Pointers must be 16-byte aligned;
- *    hidden and intermediate must be multiples of 64.
+ *    hidden and intermediate must be multiples of 64.  With bf16 storage, x
+ *    and each packed gate/up weight (one routed expert's w13, or shared_w13)
+ *    must each be smaller than 4 GiB (LBV_ERR_SHAPE otherwise).
  *  - Precision: the router weight, correction bias, routing weights and all
  *    router arithmetic are fp32.  x, expert weights, `act` and `out` use
  *    `cfg->dtype` (bf16 or fp32); expert matmuls accumulate in fp32; the

@@ -43,6 +43,12 @@ lbv_status check_cfg(const lbv_moe_config* c) {
     int epl = 1;
     while (64 * epl < c->num_experts) epl *= 2;
     if (G % epl != 0 || !is_pow2(G / epl)) return LBV_ERR_UNSUPPORTED;
+    // bf16 matmuls address their weight rows with 32-bit byte offsets
+    if (c->dtype == LBV_BF16) {
+        const int64_t w13_bytes = 2ll * c->intermediate * c->hidden * 2;
+        const int64_t shared_bytes = w13_bytes * c->n_shared_experts;
+        if (w13_bytes >= (1ll << 32) || shared_bytes >= (1ll << 32)) return LBV_ERR_SHAPE;
+    }
     return LBV_OK;
 }
 
@@ -53,6 +59,8 @@ lbv_status make_dims(const lbv_moe_config* c, int64_t T, Dims* d) {
     const int KS = c->top_k + c->n_shared_experts;
     // row indices and offsets are int32
     if (T > 0 && T > (int64_t)INT32_MAX / KS) return LBV_ERR_SHAPE;
+    // the bf16 gate/up matmul gathers rows of x with 32-bit byte offsets
+    if (c->dtype == LBV_BF16 && T * c->hidden * 2 >= (1ll << 32)) return LBV_ERR_SHAPE;
     d->T = T;
     d->H = c->hidden;
     d->E = c->num_experts;

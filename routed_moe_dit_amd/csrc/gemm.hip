@@ -15,17 +15,22 @@
 // I slice of the shared MLP, exact by linearity of the down projection).
 //
 // bf16 path: one workgroup (4 waves, 256 threads) computes a BM x BN tile of
-// one segment with v_mfma_f32_32x32x16_bf16.  A and B tiles (K-contiguous,
-// BK = 64 bf16 = 128 B per row) go global -> registers -> LDS, double-buffered
-// so the next tile's loads are in flight while the current one is multiplied.
-// LDS rows are 8 chunks of 16 B, chunk c of row r stored at c ^ (r & 7), so
-// that the 16-byte fragment reads of 8 consecutive rows hit 8 different bank
-// groups.  Tiles never cross a segment: the tile list is rebuilt from
-// `offsets` by every workgroup (no host read-back of segment sizes), and
-// the grid is sized for the worst case; surplus workgroups exit at once.
-// For the gate/up matmul a B tile holds BN/2 gate rows and the matching BN/2
-// up rows, and each wave's accumulators for gate column n and up column n sit
-// in the same lane and register, so silu(g) * u is formed in registers.
+// one segment with v_mfma_f32_32x32x16_bf16 (2 x 2 waves of 128 x 128).  A and
+// B tiles (K-contiguous, BK = 64 bf16 = 128 B per row, so every copy
+// instruction moves whole 128-byte lines) go straight from global memory to
+// LDS with global_load_lds_dwordx4 into a ring of STAGES k-tiles.  The copies
+// of the next k-tile are spread one by one between the MFMAs of the current
+// one (a burst of copies stalls the issuing wave, and with one wave per SIMD
+// that idles the matrix core); the LDS reads of slice g + 1 likewise sit
+// between the MFMAs of slice g; one barrier per k-tile hands a stage over.
+// LDS rows are 16-byte chunks, chunk c of row r stored at c ^ ((r >> 1) & 7),
+// which makes the fragment reads conflict-free.  Tiles never cross a
+// segment: the tile list is rebuilt from `offsets` by every workgroup (no
+// host read-back of segment sizes), and the grid is sized for the worst case;
+// surplus workgroups exit at once.  For the gate/up matmul a B tile holds
+// BN/2 gate rows and the matching BN/2 up rows, and each wave's accumulators
+// for gate column n and up column n sit in the same lane and register, so
+// silu(g) * u is formed in registers.
 #include <type_traits>
 
 #include "lbv_internal.h"
@@ -35,13 +40,10 @@
 // the gate/up GEMM's BN counts gate and up rows together, BN/2 act columns
 // per tile), and the k-depth BK and number STAGES of the LDS ring.
 #ifndef LBV_BK
-#define LBV_BK 32
+#define LBV_BK 64
 #endif
 #ifndef LBV_STAGES
-#define LBV_STAGES 4
-#endif
-#ifndef LBV_KK_UNROLL
-#define LBV_KK_UNROLL 2
+#define LBV_STAGES 2
 #endif
 #ifndef LBV_G1_BM
 #define LBV_G1_BM 256
@@ -166,6 +168,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     const int nt = lid % a.ntn;
     int seg, m0;
     if (!find_tile(a, BM, mt, &seg, &m0, s_tmp, s_sel)) return;
+    seg = __builtin_amdgcn_readfirstlane(seg);   // uniform (read from LDS)
+    m0 = __builtin_amdgcn_readfirstlane(m0);
 
     const int seg_r0 = a.offsets[seg];
     const int seg_n = a.offsets[seg + 1] - seg_r0;
@@ -176,49 +180,50 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     // ---- global source of each lane's 16-byte chunk (per copy instruction) ----
     // Instruction i of wave w fills LDS rows w*(rows/4) + RPI i + [0, RPI) of
     // the stage; lane l lands at row +l/CPR, physical chunk l%CPR, which holds
-    // logical chunk (l%CPR) ^ swz(row).
-    const uint16_t* aptr[AI];
-    const uint16_t* bptr[BI];
+    // logical chunk (l%CPR) ^ swz(row).  Sources are a workgroup-uniform base
+    // (scalar registers, advanced by BK per k-tile) plus a 32-bit per-lane byte
+    // offset (the host keeps every offset below 4 GiB).
+    const uint16_t* abase;
+    const uint16_t* bbase;
+    uint32_t aoff[AI], boff[BI];
+    if (MODE == 0) {
+        abase = static_cast<const uint16_t*>(a.A);
+        bbase = shared_seg ? static_cast<const uint16_t*>(a.Bsh)
+                           : static_cast<const uint16_t*>(a.B) + static_cast<int64_t>(seg) * 2 * a.I * a.H;
+    } else {
+        abase = static_cast<const uint16_t*>(a.A) + static_cast<int64_t>(seg_r0) * a.I;
+        bbase = shared_seg ? static_cast<const uint16_t*>(a.Bsh) + jsh * a.I
+                           : static_cast<const uint16_t*>(a.B) + static_cast<int64_t>(seg) * a.H * a.I;
+    }
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
         const int r = wave * (BM / 4) + i * RPI + lane / CPR;
-        const int c = (lane % CPR) ^ swz<BK>(r);
+        const uint32_t c = (lane % CPR) ^ swz<BK>(r);
         int m = m0 + r;
         if (m >= seg_n) m = seg_n - 1;
         if (MODE == 0) {
-            int64_t tok = a.rows[seg_r0 + m] / a.KS;
-            tok = tok < 0 ? 0 : (tok >= a.T ? a.T - 1 : tok);
-            aptr[i] = static_cast<const uint16_t*>(a.A) + tok * a.H + c * 8;
+            int tok = a.rows[seg_r0 + m] / a.KS;
+            tok = tok < 0 ? 0 : (tok >= a.T ? static_cast<int>(a.T) - 1 : tok);
+            aoff[i] = (static_cast<uint32_t>(tok) * static_cast<uint32_t>(a.H) + c * 8) * 2;
         } else {
-            aptr[i] = static_cast<const uint16_t*>(a.A) + static_cast<int64_t>(seg_r0 + m) * a.I +
-                      c * 8;
+            aoff[i] = (static_cast<uint32_t>(m) * static_cast<uint32_t>(a.I) + c * 8) * 2;
         }
     }
 #pragma unroll
     for (int i = 0; i < BI; ++i) {
         const int r = wave * (BN / 4) + i * RPI + lane / CPR;
-        const int c = (lane % CPR) ^ swz<BK>(r);
+        const uint32_t c = (lane % CPR) ^ swz<BK>(r);
         if (MODE == 0) {
             const int half = r / (BN / 2);
             int n = nt * (BN / 2) + (r % (BN / 2));
             if (n >= a.I) n = a.I - 1;
-            int64_t row;
-            const uint16_t* base;
-            if (!shared_seg) {
-                base = static_cast<const uint16_t*>(a.B) + static_cast<int64_t>(seg) * 2 * a.I * a.H;
-                row = half ? a.I + n : n;
-            } else {
-                base = static_cast<const uint16_t*>(a.Bsh);
-                row = half ? Is + jsh * a.I + n : jsh * a.I + n;
-            }
-            bptr[i] = base + row * a.H + c * 8;
+            const int row = shared_seg ? (half ? Is + jsh * a.I + n : jsh * a.I + n)
+                                       : (half ? a.I + n : n);
+            boff[i] = (static_cast<uint32_t>(row) * static_cast<uint32_t>(a.H) + c * 8) * 2;
         } else {
             int n = nt * BN + r;
             if (n >= a.H) n = a.H - 1;
-            bptr[i] = shared_seg
-                ? static_cast<const uint16_t*>(a.Bsh) + static_cast<int64_t>(n) * Is + jsh * a.I + c * 8
-                : static_cast<const uint16_t*>(a.B) + static_cast<int64_t>(seg) * a.H * a.I +
-                      static_cast<int64_t>(n) * a.I + c * 8;
+            boff[i] = (static_cast<uint32_t>(n) * static_cast<uint32_t>(shared_seg ? Is : a.I) + c * 8) * 2;
         }
     }
     const int a_lds = wave * (BM / 4) * BK;          // element offsets inside a stage
@@ -233,35 +238,34 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
         else if constexpr (decltype(S)::value == 2) return lds2;
         else return lds3;
     };
-    // k-tile kt into stage S: NI copy instructions per wave
-    auto issue = [&](auto S, int kt) {
-        const int k0 = kt * BK;
-        uint16_t* st = stage_buf(S);
-        const uint32_t base = lds_addr(st);
-#pragma unroll
-        for (int i = 0; i < AI; ++i)
-            lds_dma16(aptr[i] + k0, base + (a_lds + i * RPI * BK) * 2);
-#pragma unroll
-        for (int i = 0; i < BI; ++i)
-            lds_dma16(bptr[i] + k0, base + (b_lds + i * RPI * BK) * 2);
-    };
-
     // ---- fragments: weight rows are the MFMA's first operand, token rows the
     // second, so each lane ends up with 4 consecutive output columns ----------
+    constexpr int KKS = BK / 16;                 // 16-deep k-slices per stage
+    static_assert(KKS % 2 == 0, "slices alternate between two fragment sets");
     const int wm = wave >> 1, wn = wave & 1;
-    int trow[TM], wrow[TN];
+    const int khalf = lane >> 5;
+    // per-lane LDS element offsets of the fragment rows, per k-slice of a stage
+    int toff[KKS][TM], woff[KKS][TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) trow[i] = wm * (BM / 2) + i * 32 + (lane & 31);
+    for (int kk = 0; kk < KKS; ++kk) {
+        const int ch = kk * 2 + khalf;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        if (MODE == 0) {
-            constexpr int HT = TN / 2;
-            wrow[j] = (j < HT ? 0 : BN / 2) + wn * (BN / 4) + (j % HT) * 32 + (lane & 31);
-        } else {
-            wrow[j] = wn * (BN / 2) + j * 32 + (lane & 31);
+        for (int i = 0; i < TM; ++i) {
+            const int r = wm * (BM / 2) + i * 32 + (lane & 31);
+            toff[kk][i] = r * BK + ((ch ^ swz<BK>(r)) * 8);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            int r;
+            if (MODE == 0) {
+                constexpr int HT = TN / 2;
+                r = (j < HT ? 0 : BN / 2) + wn * (BN / 4) + (j % HT) * 32 + (lane & 31);
+            } else {
+                r = wn * (BN / 2) + j * 32 + (lane & 31);
+            }
+            woff[kk][j] = BM * BK + r * BK + ((ch ^ swz<BK>(r)) * 8);
         }
     }
-    const int khalf = lane >> 5;
 
     f32x16 acc[TN][TM];
 #pragma unroll
@@ -271,66 +275,146 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[j][i][q] = 0.f;
 
+    // Two fragment sets: slice g is multiplied from set g % 2 while slice g + 1
+    // is read into the other one.
+    bf16x8 tf0[TM], wf0[TN], tf1[TM], wf1[TN];
+
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
     using S2 = std::integral_constant<int, 2>;
     using S3 = std::integral_constant<int, 3>;
-    issue(S0{}, 0);
-    if constexpr (STAGES > 2) {
-        if (1 < nk) issue(S1{}, 1);
-    }
-    if constexpr (STAGES > 3) {
-        if (2 < nk) issue(S2{}, 2);
-    }
 
-    // one k-tile: wait for its stage, free the previous stage, refill it with
-    // k-tile kt + 3, multiply
-    auto step = [&](auto S, int kt) {
-        constexpr int SI = decltype(S)::value;
-        // copies of k-tile kt done; still in flight: the k-tiles issued after
-        // it (at most STAGES - 2 of them)
-        const int ahead = nk - 1 - kt;
+    // The k-loop runs over nkp = nk rounded up to a multiple of STAGES k-tiles,
+    // so that every step is unconditional (no MFMA under a branch); the k-tiles
+    // past nk are zero-filled stages, whose products add exact zeros.
+    const int nkp = (nk + STAGES - 1) / STAGES * STAGES;
+    auto zero_fill = [&](auto S) {
+        u32x4* st = reinterpret_cast<u32x4*>(stage_buf(S));
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int q = 0; q < STAGE / 8 / 256; ++q) st[tid + 256 * q] = z;
+    };
+    // copy instruction d (A rows first, then B rows) of k-tile kt into stage S
+    auto copy_one = [&](auto S, int kt, int d) {
+        const uint32_t base = lds_addr(stage_buf(S));
+        if (d < AI)
+            lds_dma16_sb(abase + kt * BK, aoff[d], base + (a_lds + d * RPI * BK) * 2);
+        else
+            lds_dma16_sb(bbase + kt * BK, boff[d - AI], base + (b_lds + (d - AI) * RPI * BK) * 2);
+    };
+    // Waits for the copies of k-tile kt when k-tiles up to `last` have been
+    // issued: the real (not zero-filled) ones after kt may stay in flight.
+    auto wait_tile = [&](int kt, int last) {
+        int ahead = (nk - 1 < last ? nk - 1 : last) - kt;
+        if (ahead < 0) ahead = 0;
         if constexpr (STAGES > 3) {
-            if (ahead >= 2) wait_vmcnt<2 * NI>();
+            if (ahead >= 3) wait_vmcnt<3 * NI>();
+            else if (ahead == 2) wait_vmcnt<2 * NI>();
             else if (ahead == 1) wait_vmcnt<NI>();
             else wait_vmcnt<0>();
         } else if constexpr (STAGES > 2) {
-            if (ahead >= 1) wait_vmcnt<NI>();
+            if (ahead >= 2) wait_vmcnt<2 * NI>();
+            else if (ahead == 1) wait_vmcnt<NI>();
             else wait_vmcnt<0>();
         } else {
-            wait_vmcnt<0>();
-        }
-        block_barrier();
-        if (kt + STAGES - 1 < nk)
-            issue(std::integral_constant<int, (SI + STAGES - 1) % STAGES>{}, kt + STAGES - 1);
-        const uint16_t* As = stage_buf(S);
-        const uint16_t* Bs = As + BM * BK;
-#pragma unroll LBV_KK_UNROLL
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            const int ch = kk * 2 + khalf;
-            bf16x8 tf[TM], wf[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                tf[i] = *reinterpret_cast<const bf16x8*>(As + trow[i] * BK + ((ch ^ swz<BK>(trow[i])) * 8));
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-                wf[j] = *reinterpret_cast<const bf16x8*>(Bs + wrow[j] * BK + ((ch ^ swz<BK>(wrow[j])) * 8));
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-                    acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], tf[i], acc[j][i], 0, 0, 0);
+            if (ahead >= 1) wait_vmcnt<NI>();
+            else wait_vmcnt<0>();
         }
     };
-    for (int kt = 0; kt < nk; kt += STAGES) {
+
+    // prologue: k-tiles 0 .. STAGES-2 into stages 0 .. STAGES-2 (each step
+    // fills the stage freed by the previous one), then the first slice read
+    auto pro_fill = [&](auto S, int kt) {
+        if (kt < nk) {
+#pragma unroll
+            for (int d = 0; d < NI; ++d) copy_one(S, kt, d);
+        } else {
+            zero_fill(S);
+        }
+    };
+    pro_fill(S0{}, 0);
+    if constexpr (STAGES > 2) pro_fill(S1{}, 1);
+    if constexpr (STAGES > 3) pro_fill(S2{}, 2);
+    wait_tile(0, STAGES - 2);
+    wait_lgkmcnt0();
+    block_barrier();
+#pragma unroll
+    for (int i = 0; i < TM; ++i) tf0[i] = *reinterpret_cast<const bf16x8*>(lds0 + toff[0][i]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) wf0[j] = *reinterpret_cast<const bf16x8*>(lds0 + woff[0][j]);
+
+    constexpr int NQ = TM * TN;                  // MFMAs per slice
+    constexpr int NPRE = 4;                      // MFMAs of the last slice before the barrier
+    constexpr int NR = TM + TN;                  // fragment reads per slice
+    static_assert(NQ >= NR + NPRE, "reads fit between the MFMAs");
+    constexpr int DSL = KKS - 1;                 // slices that carry the refill copies
+
+    // One slice: MFMAs [Q0, Q1) from set (CT, CW); after MFMA Q0 + r, fragment
+    // read r of the next slice (stage NB, slice NKK) into set (NT, NW); copy
+    // instructions [D0, D1) of k-tile KF into stage TS spread evenly over the
+    // MFMAs (when DO_COPY).  The order is pinned: one MFMA, then its read
+    // and copy, then a scheduling fence.
+#define LBV_SLICE(CT, CW, NT, NW, NB, NKK, Q0, Q1, TS, KF, DO_COPY, D0, D1)                 \
+    _Pragma("unroll") for (int q = (Q0); q < (Q1); ++q) {                                     \
+        acc[q / TM][q % TM] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                        \
+            CW[q / TM], CT[q % TM], acc[q / TM][q % TM], 0, 0, 0);                            \
+        const int r_ = q - (Q0);                                                               \
+        if (r_ < TM) NT[r_] = *reinterpret_cast<const bf16x8*>((NB) + toff[NKK][r_]);          \
+        else if (r_ < NR) NW[r_ - TM] = *reinterpret_cast<const bf16x8*>((NB) + woff[NKK][r_ - TM]); \
+        if ((D1) > (D0)) {                                                                     \
+            _Pragma("unroll") for (int d = (D0); d < (D1); ++d) {                              \
+                if ((d - (D0)) * ((Q1) - (Q0)) / ((D1) - (D0)) == r_ && (DO_COPY))              \
+                    copy_one(TS, KF, d);                                                       \
+            }                                                                                  \
+        }                                                                                      \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
+    }
+
+    // One k-tile held in stage S.  On entry slice 0 of it is in set 0.
+    // Slices 0 .. KKS-2 also carry the copies of k-tile kt + STAGES - 1 into
+    // the stage that the previous k-tile freed.  The last slice brackets the
+    // hand-over to k-tile kt + 1: NPRE MFMAs, wait for its copies, barrier
+    // (every wave is done reading stage S), then the remaining MFMAs with the
+    // reads of slice 0 of k-tile kt + 1 (unused after the last k-tile).
+    auto step = [&](auto S, int kt) {
+        constexpr int SI = decltype(S)::value;
+        const auto TS = std::integral_constant<int, (SI + STAGES - 1) % STAGES>{};
+        const uint16_t* cur = stage_buf(S);
+        const uint16_t* nxt = stage_buf(std::integral_constant<int, (SI + 1) % STAGES>{});
+        const int kf = kt + STAGES - 1;          // k-tile to copy
+        const bool do_copy = kf < nk;
+        if (!do_copy && kf < nkp) zero_fill(TS);
+#pragma unroll
+        for (int kk = 0; kk < KKS - 1; ++kk) {
+            if (kk % 2 == 0) {
+                LBV_SLICE(tf0, wf0, tf1, wf1, cur, kk + 1, 0, NQ, TS, kf, do_copy,
+                          kk * NI / DSL, (kk + 1) * NI / DSL)
+            } else {
+                LBV_SLICE(tf1, wf1, tf0, wf0, cur, kk + 1, 0, NQ, TS, kf, do_copy,
+                          kk * NI / DSL, (kk + 1) * NI / DSL)
+            }
+        }
+        // last slice (set 1)
+#pragma unroll
+        for (int q = 0; q < NPRE; ++q)
+            acc[q / TM][q % TM] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                wf1[q / TM], tf1[q % TM], acc[q / TM][q % TM], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + 1 < nkp) {
+            // issued so far: k-tiles up to kt + STAGES - 1
+            wait_tile(kt + 1, kt + STAGES - 1);
+            wait_lgkmcnt0();
+            block_barrier();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        LBV_SLICE(tf1, wf1, tf0, wf0, nxt, 0, NPRE, NQ, TS, kf, false, 0, 0)
+    };
+#undef LBV_SLICE
+    for (int kt = 0; kt < nkp; kt += STAGES) {
         step(S0{}, kt);
-        if (kt + 1 < nk) step(S1{}, kt + 1);
-        if constexpr (STAGES > 2) {
-            if (kt + 2 < nk) step(S2{}, kt + 2);
-        }
-        if constexpr (STAGES > 3) {
-            if (kt + 3 < nk) step(S3{}, kt + 3);
-        }
+        step(S1{}, kt + 1);
+        if constexpr (STAGES > 2) step(S2{}, kt + 2);
+        if constexpr (STAGES > 3) step(S3{}, kt + 3);
     }
 
     // ---- epilogue ---------------------------------------------------------------

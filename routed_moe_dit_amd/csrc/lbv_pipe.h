@@ -16,6 +16,11 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
+// Waits until every LDS access of this wave has completed.
+__device__ __forceinline__ void wait_lgkmcnt0() {
+    __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+}
+
 // Workgroup barrier without the memory fence that __syncthreads() implies (the
 // fence would wait for every load in flight, i.e. drain the prefetch queue).
 // The empty asm keeps the compiler from moving memory accesses across it.
@@ -40,6 +45,18 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t lds_base) {
         "global_load_lds_dwordx4 %1, off"
         :
         : "s"(lds_base), "v"(gsrc)
+        : "memory", "m0");
+}
+
+// Same copy with the source given as a wave-uniform 64-bit base (scalar
+// registers) plus a 32-bit per-lane byte offset.
+__device__ __forceinline__ void lds_dma16_sb(const void* sbase, uint32_t voff, uint32_t lds_base) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2"
+        :
+        : "s"(lds_base), "v"(voff), "s"(sbase)
         : "memory", "m0");
 }
 

@@ -90,6 +90,23 @@ def test_workspace_sizes():
         lbv.lbv_moe_workspace_size(c, 2 ** 31 // 9 + 1)    # row ids would overflow int32
 
 
+def test_bf16_offset_limits():
+    # bf16 matmuls address x and each packed gate/up weight with 32-bit byte offsets
+    c = lbv.config()
+    T4g = (1 << 32) // (2048 * 2)                          # x of exactly 4 GiB
+    assert lbv.lbv_moe_permute_workspace_size(c, T4g - 1) > 0
+    with pytest.raises(lbv.LbvError) as e:
+        lbv.lbv_moe_permute_workspace_size(c, T4g)
+    assert e.value.status == lbv.LBV_ERR_SHAPE
+    assert lbv.lbv_moe_permute_workspace_size(lbv.config(dtype="f32"), T4g) > 0
+    big = dict(hidden=1 << 15, intermediate=1 << 15)     # w13 of one expert: 4 GiB in bf16
+    assert lbv.lbv_moe_check_config(lbv.config(**big)) == lbv.LBV_ERR_SHAPE
+    assert lbv.lbv_moe_check_config(lbv.config(dtype="f32", **big)) == lbv.LBV_OK
+    wide = dict(hidden=1 << 15, intermediate=1 << 14, n_shared_experts=2)   # shared_w13 4 GiB
+    assert lbv.lbv_moe_check_config(lbv.config(**wide)) == lbv.LBV_ERR_SHAPE
+    assert lbv.lbv_moe_check_config(lbv.config(**dict(wide, n_shared_experts=1))) == lbv.LBV_OK
+
+
 def raw():
     return lbv.load()
 
