@@ -48,6 +48,9 @@ lbv_status check_cfg(const lbv_moe_config* c) {
         const int64_t w13_bytes = 2ll * c->intermediate * c->hidden * 2;
         const int64_t shared_bytes = w13_bytes * c->n_shared_experts;
         if (w13_bytes >= (1ll << 32) || shared_bytes >= (1ll << 32)) return LBV_ERR_SHAPE;
+        // and form row offsets with 24-bit multiplies
+        if (c->hidden >= (1 << 24) || 2ll * c->intermediate * (c->n_shared_experts > 1 ? c->n_shared_experts : 1) >= (1 << 24))
+            return LBV_ERR_SHAPE;
     }
     return LBV_OK;
 }
@@ -60,7 +63,7 @@ lbv_status make_dims(const lbv_moe_config* c, int64_t T, Dims* d) {
     // row indices and offsets are int32
     if (T > 0 && T > (int64_t)INT32_MAX / KS) return LBV_ERR_SHAPE;
     // the bf16 gate/up matmul gathers rows of x with 32-bit byte offsets
-    if (c->dtype == LBV_BF16 && T * c->hidden * 2 >= (1ll << 32)) return LBV_ERR_SHAPE;
+    if (c->dtype == LBV_BF16 && (T * c->hidden * 2 >= (1ll << 32) || T >= (1 << 24))) return LBV_ERR_SHAPE;
     d->T = T;
     d->H = c->hidden;
     d->E = c->num_experts;

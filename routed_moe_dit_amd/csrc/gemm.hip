@@ -32,18 +32,20 @@
 // for gate column n and up column n sit in the same lane and register, so
 // silu(g) * u is formed in registers.
 #include <type_traits>
+#include <utility>
 
 #include "lbv_internal.h"
 #include "lbv_pipe.h"
 
 // Compile-time shape of the bf16 path: workgroup tile BM x BN (2 x 2 waves;
 // the gate/up GEMM's BN counts gate and up rows together, BN/2 act columns
-// per tile), and the k-depth BK and number STAGES of the LDS ring.
-#ifndef LBV_BK
-#define LBV_BK 64
+// per tile); NPRE: MFMAs of a k-tile's last slice issued before its barrier;
+// COPY_SLICES: slices of a k-tile that carry the next k-tile's copies.
+#ifndef LBV_NPRE
+#define LBV_NPRE 8
 #endif
-#ifndef LBV_STAGES
-#define LBV_STAGES 2
+#ifndef LBV_COPY_SLICES
+#define LBV_COPY_SLICES 2
 #endif
 #ifndef LBV_G1_BM
 #define LBV_G1_BM 256
@@ -124,6 +126,16 @@ __device__ bool find_tile(const GemmArgs& a, int BM, int mt, int* seg_out, int* 
     return true;
 }
 
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, i>) for i = 0 .. N-1
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // 16-byte chunk swizzle of an LDS row of BK bf16: chunk c of row r is stored at
 // c ^ swz<BK>(r).  Chosen by measurement on gfx950 for the MFMA fragment read
 // (lanes 0-31 read rows r0 + lane, lanes 32-63 the next chunk), whose
@@ -136,262 +148,317 @@ __device__ __forceinline__ int swz(int r) {
     return BK == 32 ? ((r >> 2) & 3) : ((r >> 1) & 7);
 }
 
-template <int BM, int BN, int BK, int STAGES, int MODE>
+// Segments the persistent kernel's LDS tile table holds (E + n_shared <= 264).
+constexpr int kMaxSeg = 512;
+
+// Persistent bf16 grouped matmul.  The grid is a multiple of 8 workgroups, one
+// per CU; workgroup b serves XCD b % 8, which owns a contiguous eighth of the
+// logical tiles (m-tile major, ntn n-tiles per m-tile), handed to its
+// workgroups round-robin, so the tiles in flight on one XCD share operand rows
+// in its L2.  Each workgroup builds the segment tile table once, then runs
+// one continuous k-loop over all its tiles: the copies of the next tile's
+// first k-tile are issued during the current tile's last k-tile and land
+// while its epilogue runs.
+template <int BM, int BN, int MODE>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
-    // BK: bf16 per row per stage (64 or 128 bytes); STAGES: LDS ring of
-    // k-tiles, STAGES - 1 of them in flight while one is multiplied.
-    static_assert(STAGES == 2 || STAGES == 4, "2 or 4 stages");
+    constexpr int BK = 64;                       // bf16 per row per k-tile: 128 bytes
     constexpr int TM = BM / 64;                  // token tiles (32 rows) per wave
     constexpr int TN = BN / 64;                  // weight-row tiles (32 rows) per wave
     static_assert(MODE == 1 || TN % 2 == 0, "gate/up tiles come in pairs");
     constexpr int STAGE = (BM + BN) * BK;        // bf16 elements per stage
     constexpr int CPR = BK / 8;                  // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;                // rows per 1 KB copy instruction
-    constexpr int AI = BM / 4 / RPI, BI = BN / 4 / RPI;  // copies per wave per stage
+    constexpr int AI = BM / 4 / RPI, BI = BN / 4 / RPI;  // copies per wave per k-tile
     constexpr int NI = AI + BI;
+    constexpr int KKS = BK / 16;                 // 16-deep k-slices per k-tile
+    static_assert(BM / 4 == 64, "one row-id copy (64 rows) per wave");
 
-    // Four distinct LDS objects (not one array indexed by kt % 4): with the
-    // stage named at compile time the compiler can prove that a stage being
-    // read is not one being filled by the asynchronous loads, and does not
-    // drain the whole load queue before every LDS read.
-    __shared__ __attribute__((aligned(1024))) uint16_t lds0[STAGE];
-    __shared__ __attribute__((aligned(1024))) uint16_t lds1[STAGE];
-    __shared__ __attribute__((aligned(1024))) uint16_t lds2[STAGES > 2 ? STAGE : 8];
-    __shared__ __attribute__((aligned(1024))) uint16_t lds3[STAGES > 3 ? STAGE : 8];
+    // Two stages laid out [A0 | A1 | B0 | B1] (A: token rows, B: weight rows),
+    // so that a fragment read is one base register per slice plus an
+    // immediate offset below 64 KB for the stage and the row group.  Stage 1
+    // (A1 and B1) doubles as the epilogue's staging buffer.
+    constexpr int ASZ = BM * BK, BSZ = BN * BK;  // bf16 elements of one stage's A / B part
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * STAGE];
+    __shared__ int s_pre[kMaxSeg + 1];           // m-tiles before segment s
+    __shared__ int s_rid[4][64];                 // next tile's slot ids, per wave
     __shared__ int s_tmp[8];
-    __shared__ int s_sel[2];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lid = xcd_logical_block(blockIdx.x, gridDim.x);
-    const int mt = lid / a.ntn;
-    const int nt = lid % a.ntn;
-    int seg, m0;
-    if (!find_tile(a, BM, mt, &seg, &m0, s_tmp, s_sel)) return;
-    seg = __builtin_amdgcn_readfirstlane(seg);   // uniform (read from LDS)
-    m0 = __builtin_amdgcn_readfirstlane(m0);
-
-    const int seg_r0 = a.offsets[seg];
-    const int seg_n = a.offsets[seg + 1] - seg_r0;
-    const bool shared_seg = seg >= a.E;
-    const int jsh = seg - a.E;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int khalf = lane >> 5;
     const int Is = a.NS * a.I;
 
-    // ---- global source of each lane's 16-byte chunk (per copy instruction) ----
-    // Instruction i of wave w fills LDS rows w*(rows/4) + RPI i + [0, RPI) of
-    // the stage; lane l lands at row +l/CPR, physical chunk l%CPR, which holds
-    // logical chunk (l%CPR) ^ swz(row).  Sources are a workgroup-uniform base
-    // (scalar registers, advanced by BK per k-tile) plus a 32-bit per-lane byte
-    // offset (the host keeps every offset below 4 GiB).
+    // ---- segment tile table: s_pre[s] = sum over s' < s of ceil(n_s' / BM) ----
+    {
+        int c[2], inc[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int s = tid + p * 256;
+            c[p] = 0;
+            if (s < a.S) {
+                const int n = a.offsets[s + 1] - a.offsets[s];
+                c[p] = n > 0 ? (n + BM - 1) / BM : 0;
+            }
+            int v = c[p];
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int o = __shfl_up(v, off);
+                if (lane >= off) v += o;
+            }
+            inc[p] = v;
+            if (lane == 63) s_tmp[p * 4 + wave] = v;
+        }
+        __syncthreads();
+        int base0 = 0, base1 = s_tmp[0] + s_tmp[1] + s_tmp[2] + s_tmp[3];
+        for (int w = 0; w < wave; ++w) {
+            base0 += s_tmp[w];
+            base1 += s_tmp[4 + w];
+        }
+        if (tid < a.S) s_pre[tid + 1] = base0 + inc[0];
+        if (tid + 256 < a.S) s_pre[tid + 257] = base1 + inc[1];
+        if (tid == 0) s_pre[0] = 0;
+        __syncthreads();
+    }
+    const int NT = __builtin_amdgcn_readfirstlane(s_pre[a.S]) * a.ntn;
+    const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8, nslot = gridDim.x / 8;
+    const int c1 = static_cast<int>(static_cast<int64_t>(NT) * (xcd + 1) / 8);
+    int t = static_cast<int>(static_cast<int64_t>(NT) * xcd / 8) + slot;
+    if (t >= c1) return;
+
+    // ---- tile lookup: tiles are visited in increasing order, so the segment
+    // pointer only moves forward ------------------------------------------------
+    int walk = 0;
+    auto locate = [&](int tt, int& seg_, int& m0_, int& nt_) {
+        const int mt = tt / a.ntn;
+        nt_ = tt - mt * a.ntn;
+        while (__builtin_amdgcn_readfirstlane(s_pre[walk + 1]) <= mt) ++walk;
+        seg_ = walk;
+        m0_ = (mt - __builtin_amdgcn_readfirstlane(s_pre[walk])) * BM;
+    };
+
+    // ---- copy sources: a wave-uniform base (scalar registers, advanced by BK
+    // per k-tile) plus a 32-bit per-lane byte offset.  Instruction i of wave w
+    // fills LDS rows w*(rows/4) + RPI i + [0, RPI) of a stage; lane l lands at
+    // row +l/CPR, physical chunk l%CPR, which holds logical chunk
+    // (l%CPR) ^ swz(row). ---------------------------------------------------------
     const uint16_t* abase;
     const uint16_t* bbase;
     uint32_t aoff[AI], boff[BI];
-    if (MODE == 0) {
-        abase = static_cast<const uint16_t*>(a.A);
-        bbase = shared_seg ? static_cast<const uint16_t*>(a.Bsh)
-                           : static_cast<const uint16_t*>(a.B) + static_cast<int64_t>(seg) * 2 * a.I * a.H;
-    } else {
-        abase = static_cast<const uint16_t*>(a.A) + static_cast<int64_t>(seg_r0) * a.I;
-        bbase = shared_seg ? static_cast<const uint16_t*>(a.Bsh) + jsh * a.I
-                           : static_cast<const uint16_t*>(a.B) + static_cast<int64_t>(seg) * a.H * a.I;
-    }
-#pragma unroll
-    for (int i = 0; i < AI; ++i) {
-        const int r = wave * (BM / 4) + i * RPI + lane / CPR;
-        const uint32_t c = (lane % CPR) ^ swz<BK>(r);
-        int m = m0 + r;
-        if (m >= seg_n) m = seg_n - 1;
-        if (MODE == 0) {
-            int tok = a.rows[seg_r0 + m] / a.KS;
-            tok = tok < 0 ? 0 : (tok >= a.T ? static_cast<int>(a.T) - 1 : tok);
-            aoff[i] = (static_cast<uint32_t>(tok) * static_cast<uint32_t>(a.H) + c * 8) * 2;
-        } else {
-            aoff[i] = (static_cast<uint32_t>(m) * static_cast<uint32_t>(a.I) + c * 8) * 2;
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < BI; ++i) {
-        const int r = wave * (BN / 4) + i * RPI + lane / CPR;
-        const uint32_t c = (lane % CPR) ^ swz<BK>(r);
-        if (MODE == 0) {
-            const int half = r / (BN / 2);
-            int n = nt * (BN / 2) + (r % (BN / 2));
-            if (n >= a.I) n = a.I - 1;
-            const int row = shared_seg ? (half ? Is + jsh * a.I + n : jsh * a.I + n)
-                                       : (half ? a.I + n : n);
-            boff[i] = (static_cast<uint32_t>(row) * static_cast<uint32_t>(a.H) + c * 8) * 2;
-        } else {
-            int n = nt * BN + r;
-            if (n >= a.H) n = a.H - 1;
-            boff[i] = (static_cast<uint32_t>(n) * static_cast<uint32_t>(shared_seg ? Is : a.I) + c * 8) * 2;
-        }
-    }
-    const int a_lds = wave * (BM / 4) * BK;          // element offsets inside a stage
-    const int b_lds = BM * BK + wave * (BN / 4) * BK;
-
-    const int nk = a.kdim / BK;
-
-    auto stage_buf = [&](auto S) -> uint16_t* {
-        static_assert(decltype(S)::value < STAGES, "stage index");
-        if constexpr (decltype(S)::value == 0) return lds0;
-        else if constexpr (decltype(S)::value == 1) return lds1;
-        else if constexpr (decltype(S)::value == 2) return lds2;
-        else return lds3;
+    // Slot ids of this wave's 64 A rows of a tile, copied into s_rid[wave]
+    // (gate/up only; a copy like the stage copies, counted by the same waits).
+    auto rid_copy = [&](int seg_r0_, int seg_n_, int m0_) {
+        int m = m0_ + wave * 64 + lane;
+        if (m >= seg_n_) m = seg_n_ - 1;
+        lds_dma4_sb(a.rows, static_cast<uint32_t>(seg_r0_ + m) * 4, lds_addr(&s_rid[wave][0]));
     };
+    // Points the copy sources at tile (seg_, m0_, nt_); gate/up reads the slot
+    // ids from s_rid[wave], which must have landed.
+    auto set_sources = [&](int seg_, int seg_r0_, int seg_n_, int m0_, int nt_) {
+        // lane-derived terms are recomputed here rather than hoisted out of
+        // the tile loop (where they would hold registers through the k-loop)
+        const int lane = (threadIdx.x & 63) + opaque_zero();
+        const bool shared_seg = seg_ >= a.E;
+        const int jsh = seg_ - a.E;
+        if (MODE == 0) {
+            abase = static_cast<const uint16_t*>(a.A);
+            bbase = shared_seg ? static_cast<const uint16_t*>(a.Bsh)
+                               : static_cast<const uint16_t*>(a.B) + static_cast<int64_t>(seg_) * 2 * a.I * a.H;
+        } else {
+            abase = static_cast<const uint16_t*>(a.A) + static_cast<int64_t>(seg_r0_) * a.I;
+            bbase = shared_seg ? static_cast<const uint16_t*>(a.Bsh) + jsh * a.I
+                               : static_cast<const uint16_t*>(a.B) + static_cast<int64_t>(seg_) * a.H * a.I;
+        }
+#pragma unroll
+        for (int i = 0; i < AI; ++i) {
+            const int r = wave * (BM / 4) + i * RPI + lane / CPR;
+            const uint32_t c = (lane % CPR) ^ swz<BK>(r);
+            if (MODE == 0) {
+                int tok = s_rid[wave][i * RPI + lane / CPR] / a.KS;
+                tok = tok < 0 ? 0 : (tok >= a.T ? static_cast<int>(a.T) - 1 : tok);
+                aoff[i] = (__umul24(tok, a.H) + c * 8) * 2;
+            } else {
+                int m = m0_ + r;
+                if (m >= seg_n_) m = seg_n_ - 1;
+                aoff[i] = (__umul24(m, a.I) + c * 8) * 2;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < BI; ++i) {
+            const int r = wave * (BN / 4) + i * RPI + lane / CPR;
+            const uint32_t c = (lane % CPR) ^ swz<BK>(r);
+            if (MODE == 0) {
+                const int half = r / (BN / 2);
+                int n = nt_ * (BN / 2) + (r % (BN / 2));
+                if (n >= a.I) n = a.I - 1;
+                const int row = shared_seg ? (half ? Is + jsh * a.I + n : jsh * a.I + n)
+                                           : (half ? a.I + n : n);
+                boff[i] = (__umul24(row, a.H) + c * 8) * 2;
+            } else {
+                int n = nt_ * BN + r;
+                if (n >= a.H) n = a.H - 1;
+                boff[i] = (__umul24(n, shared_seg ? Is : a.I) + c * 8) * 2;
+            }
+        }
+    };
+
+    const int a_lds = wave * (BM / 4) * BK;      // this wave's rows inside an A / B part
+    const int b_lds = wave * (BN / 4) * BK;
+    const int nk = a.kdim / BK;
+    // the k-loop of a tile runs over nkp = nk rounded up to even, so that both
+    // steps of an iteration are unconditional (no MFMA under a branch); the
+    // k-tile past nk is a zero-filled stage, whose products add exact zeros
+    const int nkp = (nk + 1) & ~1;
+
+    auto a_part = [&](auto S) -> uint16_t* { return lds + decltype(S)::value * ASZ; };
+    auto b_part = [&](auto S) -> uint16_t* { return lds + 2 * ASZ + decltype(S)::value * BSZ; };
+    auto zero_fill = [&](auto S) {
+        u32x4* pa = reinterpret_cast<u32x4*>(a_part(S));
+        u32x4* pb = reinterpret_cast<u32x4*>(b_part(S));
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int q = 0; q < ASZ / 8 / 256; ++q) pa[tid + 256 * q] = z;
+#pragma unroll
+        for (int q = 0; q < BSZ / 8 / 256; ++q) pb[tid + 256 * q] = z;
+    };
+    // copy instruction D (A rows first, then B rows) of k-tile kt into stage S
+    auto copy_const = [&](auto S, int kt, auto D) {
+        constexpr int d = decltype(D)::value;
+        if constexpr (d < AI)
+            lds_dma16_sb<d * RPI * BK * 2>(abase + kt * BK, aoff[d], lds_addr(a_part(S) + a_lds));
+        else
+            lds_dma16_sb<(d - AI) * RPI * BK * 2>(bbase + kt * BK, boff[d - AI],
+                                                  lds_addr(b_part(S) + b_lds));
+    };
+    // the same for an index d that is a constant once the loops are unrolled
+    auto copy_one = [&](auto S, int kt, int d) {
+        static_for<NI>([&](auto D) {
+            if (d == decltype(D)::value) copy_const(S, kt, D);
+        });
+    };
+
     // ---- fragments: weight rows are the MFMA's first operand, token rows the
     // second, so each lane ends up with 4 consecutive output columns ----------
-    constexpr int KKS = BK / 16;                 // 16-deep k-slices per stage
-    static_assert(KKS % 2 == 0, "slices alternate between two fragment sets");
-    const int wm = wave >> 1, wn = wave & 1;
-    const int khalf = lane >> 5;
-    // per-lane LDS element offsets of the fragment rows, per k-slice of a stage
-    int toff[KKS][TM], woff[KKS][TN];
+    // A fragment i of slice kk in stage s: fa[kk] + s*ASZ + i*32*BK; B fragment
+    // j: fb[kk] + s*BSZ + brow(j)*BK.  Formed once per tile from a lane index
+    // the compiler cannot see through, so that they are not held in registers
+    // across the epilogue.
+    const uint16_t* fa[KKS];
+    const uint16_t* fb[KKS];
+    auto frag_offsets = [&]() {
+        const int ln = (threadIdx.x & 63) + opaque_zero();
+        const int kh = ln >> 5, rl = ln & 31;
+        const int ra = wm * (BM / 2) + rl;                       // first A row (i = 0)
+        const int rb = (MODE == 0 ? wn * (BN / 4) : wn * (BN / 2)) + rl;   // first B row (j = 0)
 #pragma unroll
-    for (int kk = 0; kk < KKS; ++kk) {
-        const int ch = kk * 2 + khalf;
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int r = wm * (BM / 2) + i * 32 + (lane & 31);
-            toff[kk][i] = r * BK + ((ch ^ swz<BK>(r)) * 8);
+        for (int kk = 0; kk < KKS; ++kk) {
+            const int ch = kk * 2 + kh;                          // swz(r) depends on r mod 32 only
+            fa[kk] = lds + ra * BK + ((ch ^ swz<BK>(rl)) * 8);
+            fb[kk] = lds + 2 * ASZ + rb * BK + ((ch ^ swz<BK>(rl)) * 8);
         }
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            int r;
-            if (MODE == 0) {
-                constexpr int HT = TN / 2;
-                r = (j < HT ? 0 : BN / 2) + wn * (BN / 4) + (j % HT) * 32 + (lane & 31);
-            } else {
-                r = wn * (BN / 2) + j * 32 + (lane & 31);
-            }
-            woff[kk][j] = BM * BK + r * BK + ((ch ^ swz<BK>(r)) * 8);
-        }
-    }
+    };
+    // B row of fragment j relative to j = 0
+    auto brow = [](int j) {
+        constexpr int HT = TN / 2;
+        return MODE == 0 ? (j < HT ? j * 32 : BN / 2 + (j - HT) * 32) : j * 32;
+    };
+    frag_offsets();
 
     f32x16 acc[TN][TM];
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) acc[j][i][q] = 0.f;
-
     // Two fragment sets: slice g is multiplied from set g % 2 while slice g + 1
     // is read into the other one.
     bf16x8 tf0[TM], wf0[TN], tf1[TM], wf1[TN];
 
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
-    using S2 = std::integral_constant<int, 2>;
-    using S3 = std::integral_constant<int, 3>;
 
-    // The k-loop runs over nkp = nk rounded up to a multiple of STAGES k-tiles,
-    // so that every step is unconditional (no MFMA under a branch); the k-tiles
-    // past nk are zero-filled stages, whose products add exact zeros.
-    const int nkp = (nk + STAGES - 1) / STAGES * STAGES;
-    auto zero_fill = [&](auto S) {
-        u32x4* st = reinterpret_cast<u32x4*>(stage_buf(S));
-        const u32x4 z = {0u, 0u, 0u, 0u};
+    // ---- first tile: sources, k-tile 0 into stage 0, first slice read ----------
+    int seg, m0, nt;
+    locate(t, seg, m0, nt);
+    int seg_r0 = a.offsets[seg];
+    int seg_n = a.offsets[seg + 1] - seg_r0;
+    if (MODE == 0) {
+        rid_copy(seg_r0, seg_n, m0);
+        wait_vmcnt<0>();
+    }
+    set_sources(seg, seg_r0, seg_n, m0, nt);
 #pragma unroll
-        for (int q = 0; q < STAGE / 8 / 256; ++q) st[tid + 256 * q] = z;
-    };
-    // copy instruction d (A rows first, then B rows) of k-tile kt into stage S
-    auto copy_one = [&](auto S, int kt, int d) {
-        const uint32_t base = lds_addr(stage_buf(S));
-        if (d < AI)
-            lds_dma16_sb(abase + kt * BK, aoff[d], base + (a_lds + d * RPI * BK) * 2);
-        else
-            lds_dma16_sb(bbase + kt * BK, boff[d - AI], base + (b_lds + (d - AI) * RPI * BK) * 2);
-    };
-    // Waits for the copies of k-tile kt when k-tiles up to `last` have been
-    // issued: the real (not zero-filled) ones after kt may stay in flight.
-    auto wait_tile = [&](int kt, int last) {
-        int ahead = (nk - 1 < last ? nk - 1 : last) - kt;
-        if (ahead < 0) ahead = 0;
-        if constexpr (STAGES > 3) {
-            if (ahead >= 3) wait_vmcnt<3 * NI>();
-            else if (ahead == 2) wait_vmcnt<2 * NI>();
-            else if (ahead == 1) wait_vmcnt<NI>();
-            else wait_vmcnt<0>();
-        } else if constexpr (STAGES > 2) {
-            if (ahead >= 2) wait_vmcnt<2 * NI>();
-            else if (ahead == 1) wait_vmcnt<NI>();
-            else wait_vmcnt<0>();
-        } else {
-            if (ahead >= 1) wait_vmcnt<NI>();
-            else wait_vmcnt<0>();
-        }
-    };
-
-    // prologue: k-tiles 0 .. STAGES-2 into stages 0 .. STAGES-2 (each step
-    // fills the stage freed by the previous one), then the first slice read
-    auto pro_fill = [&](auto S, int kt) {
-        if (kt < nk) {
-#pragma unroll
-            for (int d = 0; d < NI; ++d) copy_one(S, kt, d);
-        } else {
-            zero_fill(S);
-        }
-    };
-    pro_fill(S0{}, 0);
-    if constexpr (STAGES > 2) pro_fill(S1{}, 1);
-    if constexpr (STAGES > 3) pro_fill(S2{}, 2);
-    wait_tile(0, STAGES - 2);
-    wait_lgkmcnt0();
+    for (int d = 0; d < NI; ++d) copy_one(S0{}, 0, d);
+    wait_vmcnt<0>();
     block_barrier();
 #pragma unroll
-    for (int i = 0; i < TM; ++i) tf0[i] = *reinterpret_cast<const bf16x8*>(lds0 + toff[0][i]);
+    for (int i = 0; i < TM; ++i) tf0[i] = *reinterpret_cast<const bf16x8*>(fa[0] + i * 32 * BK);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) wf0[j] = *reinterpret_cast<const bf16x8*>(lds0 + woff[0][j]);
+    for (int j = 0; j < TN; ++j) wf0[j] = *reinterpret_cast<const bf16x8*>(fb[0] + brow(j) * BK);
 
     constexpr int NQ = TM * TN;                  // MFMAs per slice
-    constexpr int NPRE = 4;                      // MFMAs of the last slice before the barrier
+    constexpr int NPRE = LBV_NPRE;               // MFMAs of the last slice before the barrier
     constexpr int NR = TM + TN;                  // fragment reads per slice
     static_assert(NQ >= NR + NPRE, "reads fit between the MFMAs");
-    constexpr int DSL = KKS - 1;                 // slices that carry the refill copies
+    constexpr int DSL = LBV_COPY_SLICES < KKS - 1 ? LBV_COPY_SLICES : KKS - 1;   // slices carrying copies
 
-    // One slice: MFMAs [Q0, Q1) from set (CT, CW); after MFMA Q0 + r, fragment
-    // read r of the next slice (stage NB, slice NKK) into set (NT, NW); copy
-    // instructions [D0, D1) of k-tile KF into stage TS spread evenly over the
-    // MFMAs (when DO_COPY).  The order is pinned: one MFMA, then its read
-    // and copy, then a scheduling fence.
-#define LBV_SLICE(CT, CW, NT, NW, NB, NKK, Q0, Q1, TS, KF, DO_COPY, D0, D1)                 \
+    // One slice: MFMAs [Q0, Q1) from set (CT, CW) (ZC: the tile's first slice,
+    // accumulators start at zero); after MFMA Q0 + r, fragment read r of the
+    // next slice (stage index NB, slice NKK) into set (NT, NW); copy instructions
+    // [D0, D1) of k-tile KF into stage TS spread evenly over the MFMAs (when
+    // DO_COPY).  The order is pinned: one MFMA, then its read and copy, then
+    // a scheduling fence.
+#define LBV_SLICE(CT, CW, NT_, NW_, NB, NKK, Q0, Q1, TS, KF, DO_COPY, D0, D1, ZC)              \
     _Pragma("unroll") for (int q = (Q0); q < (Q1); ++q) {                                     \
-        acc[q / TM][q % TM] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                        \
-            CW[q / TM], CT[q % TM], acc[q / TM][q % TM], 0, 0, 0);                            \
+        if (ZC)                                                                                \
+            acc[q / TM][q % TM] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                    \
+                CW[q / TM], CT[q % TM], f32x16{}, 0, 0, 0);                                   \
+        else                                                                                   \
+            acc[q / TM][q % TM] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                    \
+                CW[q / TM], CT[q % TM], acc[q / TM][q % TM], 0, 0, 0);                        \
         const int r_ = q - (Q0);                                                               \
-        if (r_ < TM) NT[r_] = *reinterpret_cast<const bf16x8*>((NB) + toff[NKK][r_]);          \
-        else if (r_ < NR) NW[r_ - TM] = *reinterpret_cast<const bf16x8*>((NB) + woff[NKK][r_ - TM]); \
+        if (r_ < TM)                                                                           \
+            NT_[r_] = *reinterpret_cast<const bf16x8*>(fa[NKK] + (NB) * ASZ + r_ * 32 * BK);  \
+        else if (r_ < NR)                                                                      \
+            NW_[r_ - TM] = *reinterpret_cast<const bf16x8*>(fb[NKK] + (NB) * BSZ + brow(r_ - TM) * BK); \
         if ((D1) > (D0)) {                                                                     \
             _Pragma("unroll") for (int d = (D0); d < (D1); ++d) {                              \
-                if ((d - (D0)) * ((Q1) - (Q0)) / ((D1) - (D0)) == r_ && (DO_COPY))              \
+                if ((d - (D0)) * ((Q1) - (Q0)) / ((D1) > (D0) ? (D1) - (D0) : 1) == r_ && (DO_COPY)) \
                     copy_one(TS, KF, d);                                                       \
             }                                                                                  \
         }                                                                                      \
         __builtin_amdgcn_sched_barrier(0);                                                     \
     }
 
+    // Next tile (valid when has_next): its lookup is done at the start of the
+    // current tile, its slot ids are copied at step 0, its copy sources are set
+    // right after the barrier of the second-to-last step.
+    bool has_next = false;
+    int nseg = 0, nm0 = 0, nnt = 0, nseg_r0 = 0, nseg_n = 0;
+
     // One k-tile held in stage S.  On entry slice 0 of it is in set 0.
-    // Slices 0 .. KKS-2 also carry the copies of k-tile kt + STAGES - 1 into
-    // the stage that the previous k-tile freed.  The last slice brackets the
-    // hand-over to k-tile kt + 1: NPRE MFMAs, wait for its copies, barrier
-    // (every wave is done reading stage S), then the remaining MFMAs with the
-    // reads of slice 0 of k-tile kt + 1 (unused after the last k-tile).
-    auto step = [&](auto S, int kt) {
+    // Slices 0 .. DSL-1 also carry the copies of k-tile kt + 1 (or, at the last
+    // k-tile, of the next tile's k-tile 0) into the other stage, which the
+    // previous k-tile freed.  The last slice brackets the hand-over: NPRE
+    // MFMAs, wait for k-tile kt + 1's copies, barrier (every wave is done
+    // reading stage S), then the remaining MFMAs with the reads of slice 0 of
+    // k-tile kt + 1 (unused after the tile's last k-tile).
+    auto step = [&](auto S, int kt, auto First) {
         constexpr int SI = decltype(S)::value;
-        const auto TS = std::integral_constant<int, (SI + STAGES - 1) % STAGES>{};
-        const uint16_t* cur = stage_buf(S);
-        const uint16_t* nxt = stage_buf(std::integral_constant<int, (SI + 1) % STAGES>{});
-        const int kf = kt + STAGES - 1;          // k-tile to copy
-        const bool do_copy = kf < nk;
-        if (!do_copy && kf < nkp) zero_fill(TS);
+        constexpr bool FIRST = decltype(First)::value;
+        const auto TS = std::integral_constant<int, 1 - SI>{};
+        constexpr int cur = SI, nxt = 1 - SI;   // stages read by this k-tile / the next
+        const int kf = kt + 1;
+        const bool last = kf == nkp;
+        const bool do_copy = kf < nk || (last && has_next);
+        const int kc = last ? 0 : kf;            // k-tile index of the copies
+        if (kf >= nk && !last) zero_fill(TS);
+        if (MODE == 0 && kt == 0 && has_next) rid_copy(nseg_r0, nseg_n, nm0);
 #pragma unroll
         for (int kk = 0; kk < KKS - 1; ++kk) {
             if (kk % 2 == 0) {
-                LBV_SLICE(tf0, wf0, tf1, wf1, cur, kk + 1, 0, NQ, TS, kf, do_copy,
-                          kk * NI / DSL, (kk + 1) * NI / DSL)
+                LBV_SLICE(tf0, wf0, tf1, wf1, cur, kk + 1, 0, NQ, TS, kc, do_copy && kk < DSL,
+                          kk < DSL ? kk * NI / DSL : 0, kk < DSL ? (kk + 1) * NI / DSL : 0,
+                          FIRST && kk == 0)
             } else {
-                LBV_SLICE(tf1, wf1, tf0, wf0, cur, kk + 1, 0, NQ, TS, kf, do_copy,
-                          kk * NI / DSL, (kk + 1) * NI / DSL)
+                LBV_SLICE(tf1, wf1, tf0, wf0, cur, kk + 1, 0, NQ, TS, kc, do_copy && kk < DSL,
+                          kk < DSL ? kk * NI / DSL : 0, kk < DSL ? (kk + 1) * NI / DSL : 0,
+                          false)
             }
         }
         // last slice (set 1)
@@ -400,83 +467,124 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
             acc[q / TM][q % TM] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 wf1[q / TM], tf1[q % TM], acc[q / TM][q % TM], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        if (kt + 1 < nkp) {
-            // issued so far: k-tiles up to kt + STAGES - 1
-            wait_tile(kt + 1, kt + STAGES - 1);
+        if (!last) wait_vmcnt<0>();              // k-tile kt + 1 (and any slot-id copy) landed
+        wait_lgkmcnt0();
+        block_barrier();
+        if (kf == nkp - 1 && has_next) {
+            set_sources(nseg, nseg_r0, nseg_n, nm0, nnt);
             wait_lgkmcnt0();
-            block_barrier();
         }
         __builtin_amdgcn_sched_barrier(0);
-        LBV_SLICE(tf1, wf1, tf0, wf0, nxt, 0, NPRE, NQ, TS, kf, false, 0, 0)
+        LBV_SLICE(tf1, wf1, tf0, wf0, nxt, 0, NPRE, NQ, TS, kc, false, 0, 0, false)
     };
 #undef LBV_SLICE
-    for (int kt = 0; kt < nkp; kt += STAGES) {
-        step(S0{}, kt);
-        step(S1{}, kt + 1);
-        if constexpr (STAGES > 2) step(S2{}, kt + 2);
-        if constexpr (STAGES > 3) step(S3{}, kt + 3);
-    }
 
-    // ---- epilogue ---------------------------------------------------------------
-    // Lane holds, for token tile i and weight tile j, output columns
-    // 8q + 4*khalf + [0, 4) of token row (lane & 31).  Each wave first writes
-    // its tile as bf16 into its own LDS region (row pitch = its column count,
-    // 16-byte chunks XOR-swizzled by row), then reads it back 16 bytes per lane
-    // so that every global store instruction writes whole contiguous rows.
     constexpr int WCOLS = MODE == 0 ? BN / 4 : BN / 2;   // output columns per wave
     constexpr int CHUNKS = WCOLS / 8;                    // 16-byte chunks per row
-    block_barrier();                                     // all waves done with the stages
-    uint16_t* ep;                                        // this wave's region (128 x WCOLS)
-    if constexpr (STAGES == 4) {
-        static_assert(128 * WCOLS <= STAGE, "one wave tile per stage buffer");
-        ep = wave == 0 ? lds0 : wave == 1 ? lds1 : wave == 2 ? lds2 : lds3;
-    } else {
-        static_assert(STAGES == 2 && 2 * 128 * WCOLS <= STAGE, "two wave tiles per stage buffer");
-        ep = ((wave & 1) ? lds1 : lds0) + (wave >> 1) * 128 * WCOLS;
-    }
+    constexpr int PROWS = 8192 / WCOLS;                  // rows per staging pass (16 KB per wave)
+    constexpr int PT = PROWS / 32;                       // token tiles per pass
+    static_assert(2 * 8192 <= ASZ && 2 * 8192 <= BSZ, "staging fits in stage 1");
+    uint16_t* const ep0 = (wave < 2 ? lds + ASZ : lds + 2 * ASZ + BSZ) + (wave & 1) * 8192;   // this wave's staging region
     auto ep_off = [&](int row, int col) {                // element offset of (row, col) in the region
         return row * WCOLS + (((col >> 3) ^ (row % CHUNKS)) << 3) + (col & 7);
     };
+    uint16_t* C = static_cast<uint16_t*>(a.C);
+    const int ncols = MODE == 0 ? a.I : a.H;
+
+    for (;;) {
+        const int tn = t + nslot;
+        has_next = tn < c1;
+        if (has_next) {
+            locate(tn, nseg, nm0, nnt);
+            nseg_r0 = a.offsets[nseg];
+            nseg_n = a.offsets[nseg + 1] - nseg_r0;
+        }
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int row = i * 32 + (lane & 31);
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int j = 0; j < (MODE == 0 ? TN / 2 : TN); ++j) {
+            for (int i = 0; i < TM; ++i) acc[j][i] = f32x16{};
+        for (int kt = 0; kt < nkp; kt += 2) {
+            step(S0{}, kt, std::false_type{});
+            step(S1{}, kt + 1, std::false_type{});
+        }
+
+        // ---- epilogue: lane holds, for token tile i and weight tile j, output
+        // columns 8q + 4*khalf + [0, 4) of token row (lane & 31).  Each wave
+        // writes PROWS rows of its tile as bf16 into its staging region (row
+        // pitch = its column count, 16-byte chunks XOR-swizzled by row), then
+        // reads them back 16 bytes per lane, so that every global store
+        // instruction writes whole contiguous rows.  Every wave passed the last
+        // barrier after its final reads of stage 1.
+        const int col0 = MODE == 0 ? nt * (BN / 2) + wn * (BN / 4) : nt * BN + wn * (BN / 2);
+        // staging addresses are formed here, not hoisted out of the tile loop
+        // (where they would hold registers through the whole k-loop)
+        uint16_t* const ep = ep0;
+        const int elane = (threadIdx.x & 63) + opaque_zero();
+        const int ekh = elane >> 5;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int col = j * 32 + 8 * q + 4 * khalf;
-                float v[4];
+        for (int p = 0; p < TM / PT; ++p) {
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    if (MODE == 0) {
-                        const float g = acc[j][i][4 * q + p];
-                        const float u = acc[j + TN / 2][i][4 * q + p];
-                        v[p] = g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-                    } else {
-                        v[p] = acc[j][i][4 * q + p];
+            for (int ii = 0; ii < PT; ++ii) {
+                const int i = p * PT + ii;
+                const int row = ii * 32 + (elane & 31);
+#pragma unroll
+                for (int j = 0; j < (MODE == 0 ? TN / 2 : TN); ++j) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int col = j * 32 + 8 * q + 4 * ekh;
+                        float v[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            if (MODE == 0) {
+                                const float g = acc[j][i][4 * q + e];
+                                const float u = acc[j + TN / 2][i][4 * q + e];
+                                v[e] = g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+                            } else {
+                                v[e] = acc[j][i][4 * q + e];
+                            }
+                        }
+                        uint2 o;
+                        o.x = pack_bf16x2(v[0], v[1]);
+                        o.y = pack_bf16x2(v[2], v[3]);
+                        *reinterpret_cast<uint2*>(ep + ep_off(row, col)) = o;
                     }
+                    __builtin_amdgcn_sched_barrier(0);   // bounds the accumulators read out at once
                 }
-                uint2 o;
-                o.x = pack_bf16x2(v[0], v[1]);
-                o.y = pack_bf16x2(v[2], v[3]);
-                *reinterpret_cast<uint2*>(ep + ep_off(row, col)) = o;
+            }
+            if (p == 0) wait_vmcnt<0>();             // the next tile's k-tile 0 landed
+            // read back: lane -> (row, chunk); an instruction covers 64 / CHUNKS rows
+            constexpr int RPP = 64 / CHUNKS;
+#pragma unroll
+            for (int r0 = 0; r0 < PROWS; r0 += RPP) {
+                const int row = r0 + elane / CHUNKS;
+                const int ch = elane % CHUNKS;
+                const int m = m0 + wm * (BM / 2) + p * PROWS + row;
+                const int col = col0 + ch * 8;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(ep + ep_off(row, ch * 8));
+                if (m < seg_n && col < ncols)
+                    *reinterpret_cast<u32x4*>(C + static_cast<int64_t>(seg_r0 + m) * ncols + col) = v;
             }
         }
-    }
-    // read back: lane -> (row, chunk); a pass covers 64 / CHUNKS rows
-    const int ncols = MODE == 0 ? a.I : a.H;
-    const int col0 = MODE == 0 ? nt * (BN / 2) + wn * (BN / 4) : nt * BN + wn * (BN / 2);
-    uint16_t* C = static_cast<uint16_t*>(a.C);
-    constexpr int RPP = 64 / CHUNKS;                     // rows per pass
-#pragma unroll 4
-    for (int r0 = 0; r0 < 128; r0 += RPP) {
-        const int row = r0 + lane / CHUNKS;
-        const int ch = lane % CHUNKS;
-        const int m = m0 + wm * (BM / 2) + row;
-        const int col = col0 + ch * 8;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(ep + ep_off(row, ch * 8));
-        if (m < seg_n && col < ncols)
-            *reinterpret_cast<u32x4*>(C + static_cast<int64_t>(seg_r0 + m) * ncols + col) = v;
+        if (!has_next) break;
+        // every wave done with its staging reads (stage 1 may be refilled) and
+        // every wave's copies of the next tile's k-tile 0 landed
+        wait_lgkmcnt0();
+        block_barrier();
+        // the next tile's copy sources again (they were set for its k-tile 0
+        // copies before the epilogue; re-forming them here keeps them out of
+        // the epilogue's registers), and the fragment offsets
+        set_sources(nseg, nseg_r0, nseg_n, nm0, nnt);
+        frag_offsets();
+#pragma unroll
+        for (int i = 0; i < TM; ++i) tf0[i] = *reinterpret_cast<const bf16x8*>(fa[0] + i * 32 * BK);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) wf0[j] = *reinterpret_cast<const bf16x8*>(fb[0] + brow(j) * BK);
+        t = tn;
+        seg = nseg;
+        m0 = nm0;
+        nt = nnt;
+        seg_r0 = nseg_r0;
+        seg_n = nseg_n;
     }
 }
 
@@ -647,6 +755,20 @@ __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
 constexpr int G1_BM = LBV_G1_BM, G1_BN = LBV_G1_BN;
 constexpr int G2_BM = LBV_G2_BM, G2_BN = LBV_G2_BN;
 
+// Workgroups of the persistent bf16 kernels: one per CU, a multiple of 8.
+int persistent_grid() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cached[dev] == 0) {
+        int cu = 0;
+        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu < 8)
+            cu = 256;
+        cached[dev] = cu / 8 * 8;
+    }
+    return cached[dev];
+}
+
 GemmArgs make_args(const Dims& d) {
     GemmArgs a;
     a.T = d.T;
@@ -679,9 +801,8 @@ hipError_t launch_gemm_w13(const Dims& d, const void* x, const void* w13,
     a.ncols = d.I;
     if (d.bf16) {
         a.ntn = (d.I + G1_BN / 2 - 1) / (G1_BN / 2);
-        const int64_t grid = max_mtiles(d, G1_BM) * a.ntn;
-        hipLaunchKernelGGL((gemm_bf16_kernel<G1_BM, G1_BN, LBV_BK, LBV_STAGES, 0>),
-                           dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((gemm_bf16_kernel<G1_BM, G1_BN, 0>), dim3(persistent_grid()), dim3(256),
+                           0, stream, a);
     } else {
         a.ntn = (d.I + 31) / 32;
         const int64_t grid = max_mtiles(d, 32) * a.ntn;
@@ -704,9 +825,8 @@ hipError_t launch_gemm_w2(const Dims& d, const void* act, const void* w2, const 
     a.ncols = d.H;
     if (d.bf16) {
         a.ntn = (d.H + G2_BN - 1) / G2_BN;
-        const int64_t grid = max_mtiles(d, G2_BM) * a.ntn;
-        hipLaunchKernelGGL((gemm_bf16_kernel<G2_BM, G2_BN, LBV_BK, LBV_STAGES, 1>),
-                           dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((gemm_bf16_kernel<G2_BM, G2_BN, 1>), dim3(persistent_grid()), dim3(256),
+                           0, stream, a);
     } else {
         a.ntn = (d.H + 31) / 32;
         const int64_t grid = max_mtiles(d, 32) * a.ntn;

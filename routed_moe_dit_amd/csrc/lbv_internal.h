@@ -74,6 +74,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// Zero that the compiler cannot see through: a value derived from it is
+// formed where it is written (the memory clobber also keeps it from moving
+// across the surrounding loads and stores).
+__device__ __forceinline__ int opaque_zero() {
+    int z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z) : : "memory");
+    return z;
+}
+
 // Workgroups are handed to the 8 XCDs round-robin (block b runs on XCD b % 8).
 // Renumber them so that each XCD walks a contiguous range of logical tiles:
 // neighbouring tiles (which share operand rows) then meet in the same L2.

@@ -49,12 +49,26 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t lds_base) {
 }
 
 // Same copy with the source given as a wave-uniform 64-bit base (scalar
-// registers) plus a 32-bit per-lane byte offset.
+// registers) plus a 32-bit per-lane byte offset, and the LDS destination as a
+// wave-uniform base plus a compile-time byte offset.
+template <uint32_t LDS_OFF>
 __device__ __forceinline__ void lds_dma16_sb(const void* sbase, uint32_t voff, uint32_t lds_base) {
+    asm volatile(
+        "s_add_u32 m0, %0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2"
+        :
+        : "s"(lds_base), "v"(voff), "s"(sbase), "i"(LDS_OFF)
+        : "memory", "m0", "scc");
+}
+
+// 4-byte-per-lane variant (global_load_lds_dword): lane l's word lands at
+// LDS byte address lds_base + 4 l.
+__device__ __forceinline__ void lds_dma4_sb(const void* sbase, uint32_t voff, uint32_t lds_base) {
     asm volatile(
         "s_mov_b32 m0, %0\n\t"
         "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, %2"
+        "global_load_lds_dword %1, %2"
         :
         : "s"(lds_base), "v"(voff), "s"(sbase)
         : "memory", "m0");
