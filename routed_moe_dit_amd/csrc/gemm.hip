@@ -32,7 +32,6 @@
 // for gate column n and up column n sit in the same lane and register, so
 // silu(g) * u is formed in registers.
 #include <type_traits>
-#include <utility>
 
 #include "lbv_internal.h"
 #include "lbv_pipe.h"
@@ -124,16 +123,6 @@ __device__ bool find_tile(const GemmArgs& a, int BM, int mt, int* seg_out, int* 
     *seg_out = seg;
     *m0_out = (mt - s_sel[1]) * BM;
     return true;
-}
-
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
-    (f(std::integral_constant<int, I>{}), ...);
-}
-// f(integral_constant<int, i>) for i = 0 .. N-1
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-    static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // 16-byte chunk swizzle of an LDS row of BK bf16: chunk c of row r is stored at
@@ -683,7 +672,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Combine: one wave per token, 8 consecutive outputs per lane per step.
+// Combine: one wave per token; per step a lane owns 16 contiguous bytes of the
+// output row and first issues the loads of all the token's slot rows at once
+// (the step is bound by HBM latency and bandwidth), then sums them in slot
+// order in fp32 and rounds once.
 // ---------------------------------------------------------------------------
 struct CombArgs {
     const void* y;
@@ -697,9 +689,11 @@ struct CombArgs {
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
     const int lane = threadIdx.x & 63;
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (t >= a.T) return;
     constexpr int MAXS = 24;   // K <= 16 plus up to 8 shared pseudo-experts
+    constexpr int EPL = BF16 ? 8 : 4;            // elements per lane per step (16 bytes)
+    constexpr int ESZ = BF16 ? 2 : 4;
     int rows[MAXS];
     float wt[MAXS];
 #pragma unroll
@@ -711,63 +705,47 @@ __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
             if (k < a.K) wt[k] = a.w[t * a.K + k];
         }
     }
-    for (int h0 = lane * 8; h0 < a.H; h0 += 512) {
-        float acc[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    const char* y = static_cast<const char*>(a.y);
+    for (int h0 = lane * EPL; h0 < a.H; h0 += 64 * EPL) {
+        u32x4 q[MAXS];
 #pragma unroll
         for (int k = 0; k < MAXS; ++k) {
-            const int r = rows[k];
-            if (r < 0) continue;
-            if (BF16) {
-                const uint4 q = *reinterpret_cast<const uint4*>(
-                    static_cast<const uint16_t*>(a.y) + static_cast<int64_t>(r) * a.H + h0);
-                const uint32_t qq[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    acc[2 * i] += wt[k] * __uint_as_float(qq[i] << 16);
-                    acc[2 * i + 1] += wt[k] * __uint_as_float(qq[i] & 0xffff0000u);
-                }
-            } else {
-                const float4* p = reinterpret_cast<const float4*>(
-                    static_cast<const float*>(a.y) + static_cast<int64_t>(r) * a.H + h0);
-                const float4 p0 = p[0], p1 = p[1];
-                const float v[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] += wt[k] * v[i];
+            if (k < a.KS) {
+                const int r = rows[k] < 0 ? 0 : rows[k];   // unused when the slot is empty
+                q[k] = *reinterpret_cast<const u32x4*>(y + (static_cast<int64_t>(r) * a.H + h0) * ESZ);
             }
         }
-        if (BF16) {
-            uint4 o;
-            o.x = pack_bf16x2(acc[0], acc[1]);
-            o.y = pack_bf16x2(acc[2], acc[3]);
-            o.z = pack_bf16x2(acc[4], acc[5]);
-            o.w = pack_bf16x2(acc[6], acc[7]);
-            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + t * a.H + h0) = o;
-        } else {
-            float4* p = reinterpret_cast<float4*>(static_cast<float*>(a.out) + t * a.H + h0);
-            p[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-            p[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        float acc[EPL];
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) acc[i] = 0.f;
+#pragma unroll
+        for (int k = 0; k < MAXS; ++k) {
+            if (k < a.KS && rows[k] >= 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (BF16) {
+                        acc[2 * i] += wt[k] * __uint_as_float(q[k][i] << 16);
+                        acc[2 * i + 1] += wt[k] * __uint_as_float(q[k][i] & 0xffff0000u);
+                    } else {
+                        acc[i] += wt[k] * __uint_as_float(q[k][i]);
+                    }
+                }
+            }
         }
+        u32x4 o;
+        if (BF16) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(acc[i]);
+        }
+        *reinterpret_cast<u32x4*>(static_cast<char*>(a.out) + (t * a.H + h0) * ESZ) = o;
     }
 }
 
 constexpr int G1_BM = LBV_G1_BM, G1_BN = LBV_G1_BN;
 constexpr int G2_BM = LBV_G2_BM, G2_BN = LBV_G2_BN;
-
-// Workgroups of the persistent bf16 kernels: one per CU, a multiple of 8.
-int persistent_grid() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (cached[dev] == 0) {
-        int cu = 0;
-        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu < 8)
-            cu = 256;
-        cached[dev] = cu / 8 * 8;
-    }
-    return cached[dev];
-}
 
 GemmArgs make_args(const Dims& d) {
     GemmArgs a;
@@ -801,7 +779,7 @@ hipError_t launch_gemm_w13(const Dims& d, const void* x, const void* w13,
     a.ncols = d.I;
     if (d.bf16) {
         a.ntn = (d.I + G1_BN / 2 - 1) / (G1_BN / 2);
-        hipLaunchKernelGGL((gemm_bf16_kernel<G1_BM, G1_BN, 0>), dim3(persistent_grid()), dim3(256),
+        hipLaunchKernelGGL((gemm_bf16_kernel<G1_BM, G1_BN, 0>), dim3(cu_count() / 8 * 8), dim3(256),
                            0, stream, a);
     } else {
         a.ntn = (d.I + 31) / 32;
@@ -825,7 +803,7 @@ hipError_t launch_gemm_w2(const Dims& d, const void* act, const void* w2, const 
     a.ncols = d.H;
     if (d.bf16) {
         a.ntn = (d.H + G2_BN - 1) / G2_BN;
-        hipLaunchKernelGGL((gemm_bf16_kernel<G2_BM, G2_BN, 1>), dim3(persistent_grid()), dim3(256),
+        hipLaunchKernelGGL((gemm_bf16_kernel<G2_BM, G2_BN, 1>), dim3(cu_count() / 8 * 8), dim3(256),
                            0, stream, a);
     } else {
         a.ntn = (d.H + 31) / 32;

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace lbv {
 
 // ---------------------------------------------------------------------------
@@ -29,6 +31,21 @@ struct Dims {
     float rsf;      // routed_scaling_factor
     int bf16;       // 1: bf16 storage, 0: fp32 storage
 };
+
+// Compute units of the current device (cached per device; 256 if the query
+// fails).
+inline int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cached[dev] == 0) {
+        int cu = 0;
+        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu < 8)
+            cu = 256;
+        cached[dev] = cu;
+    }
+    return cached[dev];
+}
 
 // Launchers (all enqueue on `stream`, return hipGetLastError()).
 size_t route_ws_bytes(const Dims& d);
@@ -72,6 +89,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     const f32x2_t v = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, i>) for i = 0 .. N-1
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // Zero that the compiler cannot see through: a value derived from it is

@@ -11,7 +11,8 @@
 //              lane mask of the wave's tokens that chose the expert (LDS
 //              ds_or_b64), and writes its per-expert token counts.
 //  2. scan:    one block turns the counts into per-block starting offsets and
-//              the segment offsets (shared pseudo-experts own T rows each).
+//              the segment offsets (shared pseudo-experts own T rows each);
+//              a thread per expert walks its column of block counts.
 //  3. scatter: every block rebuilds its masks; a token's rank inside its
 //              expert's block range is the popcount of the lower lanes' bits
 //              plus the counts of the lower waves, so the order is by token.
@@ -102,14 +103,22 @@ __global__ __launch_bounds__(PB) void perm_scan_kernel(PermArgs a) {
     __shared__ int tmp[4];
     const int tid = threadIdx.x;
     // per expert: block offsets (in place) and the expert's total
+    // (chunks of 16 independent loads, so that the column is not walked one
+    // memory latency per block)
     int total_e = 0;
     if (tid < a.E) {
+        constexpr int CH = 16;
         int run = 0;
-        for (int b = 0; b < a.nb; ++b) {
-            int32_t* p = a.blk + static_cast<int64_t>(b) * a.E + tid;
-            const int c = *p;
-            *p = run;
-            run += c;
+        for (int b0 = 0; b0 < a.nb; b0 += CH) {
+            int c[CH];
+#pragma unroll
+            for (int i = 0; i < CH; ++i)
+                c[i] = b0 + i < a.nb ? a.blk[static_cast<int64_t>(b0 + i) * a.E + tid] : 0;
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+                if (b0 + i < a.nb) a.blk[static_cast<int64_t>(b0 + i) * a.E + tid] = run;
+                run += c[i];
+            }
         }
         total_e = run;
     }

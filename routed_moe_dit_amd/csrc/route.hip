@@ -289,19 +289,20 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
 // bf16, so each product x*plane is exact in fp32 and the MFMA sums them in
 // fp32: the logit is an fp32 dot product, in a different summation order.
 //
-// One workgroup routes 128 tokens.  Per 32-wide hidden slice a stage holds the
-// 128 x rows and the 3 x EP plane rows (64 bytes each), filled by
-// asynchronous copies three slices ahead.  Wave w owns expert tile w (32
-// experts) against all 4 token tiles: 3 planes x 4 = 12 MFMAs per 16-deep
-// step.  The epilogue turns logits into scores s = sigmoid(z) and selection
-// values c = s + bias in LDS; then each lane routes one token by scanning
-// its row: in-group top-2 sums, kept groups, and a sorted top-K insertion in
-// (c descending, id ascending) order over the kept groups' experts.
+// One workgroup routes TOK = 32 TM tokens (TM chosen per call so that the
+// grid fills the CUs in one round where it can).  Per 64-wide hidden slice a
+// stage holds the TOK x rows and the 3 x EP plane rows (128 bytes each, laid
+// out [X0|X1|W0|W1] over two stages), filled by asynchronous copies that are
+// spread one by one between the MFMAs of the previous slice.  Wave w owns
+// expert tile w % (EP/32) (32 experts) against all TM token tiles: 3 planes x
+// TM MFMAs per 16-deep step.  The epilogue turns logits into scores
+// s = sigmoid(z) in LDS; then each lane routes one token by scanning its row
+// with selection values c = s + bias: in-group top-2 sums, kept groups, and a
+// sorted top-K insertion in (c descending, id ascending) order over the kept
+// groups' experts.
 
-constexpr int RV_TOK = 128;
-constexpr int RV_BK = 32;
-constexpr int RV_STAGES = 4;
 constexpr int RV_NGMAX = 8;
+constexpr int RV_BK = 64;
 
 struct RouteV2Args {
     const uint16_t* x;       // [T, H] bf16
@@ -329,129 +330,186 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* wr, uint
     planes[2 * n + i] = f32_to_bf16(r2);
 }
 
-__device__ __forceinline__ int rswz(int r) { return (r >> 2) & 3; }   // 64-byte rows
+// 128-byte rows: chunk c of row r at c ^ ((r >> 1) & 7) (conflict-free reads)
+__device__ __forceinline__ int rswz(int r) { return (r >> 1) & 7; }
 
-template <int EP, int KMAX>
+template <int TM, int EP, int KMAX>
 __global__ __launch_bounds__(256) void route_bf16_kernel(RouteV2Args a) {
     typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
     typedef float f32x16 __attribute__((ext_vector_type(16)));
-    constexpr int ROWS = RV_TOK + 3 * EP;                 // stage rows
-    constexpr int STAGE = ROWS * RV_BK;                   // bf16 elements
-    constexpr int NI = ROWS / 64;                         // copies per wave per stage (16 rows each)
-    static_assert(ROWS % 64 == 0, "stage rows split over 4 waves");
-    constexpr int PITCH = EP + 4;                         // floats per token row of c / s
-    constexpr int STAGE_BYTES = RV_STAGES * STAGE * 2;
-    constexpr int CS_BYTES = 2 * RV_TOK * PITCH * 4;
-    constexpr int SMEM = STAGE_BYTES > CS_BYTES ? STAGE_BYTES : CS_BYTES;
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    constexpr int BK = RV_BK;
+    constexpr int TOK = 32 * TM;
+    constexpr int XSZ = TOK * BK, WSZ = 3 * EP * BK;      // bf16 elements of one stage's parts
+    constexpr int XI = TOK / 4 / 8, WI = 3 * EP / 4 / 8;  // copies per wave per k-tile (8 rows each)
+    constexpr int NI = XI + WI;
+    static_assert(TOK % 32 == 0 && (3 * EP) % 32 == 0, "rows split over 4 waves in 8-row copies");
+    constexpr int PITCH = EP + 4;                         // floats per token row of s
+    constexpr int SMEM = 2 * (XSZ + WSZ) * 2;
+    static_assert(TOK * PITCH * 4 <= SMEM, "scores fit in the stage memory");
     __shared__ __attribute__((aligned(1024))) uint16_t smem[SMEM / 2];
+    __shared__ float s_bias[EP];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * RV_TOK;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TOK;
     const int H = a.H, E = a.E;
+    if (tid < EP) s_bias[tid] = tid < E ? a.bias[tid] : 0.f;
 
-    // ---- copy sources: instruction i of this wave fills stage rows
-    // wave * (ROWS/4) + 16 i + lane/4, logical chunk (lane%4) ^ rswz(row) ----
-    const uint16_t* src[NI];
+    // ---- copy sources: a uniform base plus 32-bit per-lane byte offsets.  X
+    // copy i of wave w fills x rows w*TOK/4 + 8i + lane/8; W copy i fills plane
+    // rows w*3EP/4 + 8i + lane/8 (plane p = row / EP, expert row % EP); lane l
+    // lands at physical chunk l%8, which holds logical chunk (l%8) ^ rswz(row).
+    uint32_t xoff[XI], woff[WI];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        const int r = wave * (ROWS / 4) + i * 16 + (lane >> 2);
-        const int c = (lane & 3) ^ rswz(r);
-        if (r < RV_TOK) {
-            int64_t t = t0 + r;
-            if (t >= a.T) t = a.T - 1;
-            src[i] = a.x + t * H + c * 8;
-        } else {
-            const int q = r - RV_TOK;
-            const int p = q / EP;
-            int e = q % EP;
-            if (e >= E) e = E - 1;
-            src[i] = a.planes + (static_cast<int64_t>(p) * E + e) * H + c * 8;
-        }
+    for (int i = 0; i < XI; ++i) {
+        const int r = wave * (TOK / 4) + i * 8 + (lane >> 3);
+        const uint32_t c = (lane & 7) ^ rswz(r);
+        int64_t t = t0 + r;
+        if (t >= a.T) t = a.T - 1;
+        xoff[i] = (__umul24(static_cast<uint32_t>(t), H) + c * 8) * 2;
     }
-    auto issue = [&](int kt) {
-        const uint32_t base = lds_addr(smem + (kt % RV_STAGES) * STAGE);
 #pragma unroll
-        for (int i = 0; i < NI; ++i)
-            lds_dma16(src[i] + kt * RV_BK, base + (wave * (ROWS / 4) + i * 16) * RV_BK * 2);
+    for (int i = 0; i < WI; ++i) {
+        const int q = wave * (3 * EP / 4) + i * 8 + (lane >> 3);
+        const uint32_t c = (lane & 7) ^ rswz(q);
+        const int p = q / EP;
+        int e = q % EP;
+        if (e >= E) e = E - 1;
+        woff[i] = (__umul24(p * E + e, H) + c * 8) * 2;
+    }
+    uint16_t* const xs = smem;                            // X0, X1
+    uint16_t* const ws = smem + 2 * XSZ;                  // W0, W1
+    auto copies = [&](auto S, int kt, int d0, int d1) {
+        constexpr int s = decltype(S)::value;
+        static_for<NI>([&](auto D) {
+            constexpr int d = decltype(D)::value;
+            if (d >= d0 && d < d1) {
+                if constexpr (d < XI)
+                    lds_dma16_sb<d * 8 * BK * 2>(a.x + kt * BK, xoff[d],
+                                                 lds_addr(xs + s * XSZ + wave * (TOK / 4) * BK));
+                else
+                    lds_dma16_sb<(d - XI) * 8 * BK * 2>(a.planes + kt * BK, woff[d - XI],
+                                                        lds_addr(ws + s * WSZ + wave * (3 * EP / 4) * BK));
+            }
+        });
+    };
+    auto zero_fill = [&](auto S) {
+        constexpr int s = decltype(S)::value;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        u32x4* px = reinterpret_cast<u32x4*>(xs + s * XSZ);
+        u32x4* pw = reinterpret_cast<u32x4*>(ws + s * WSZ);
+        for (int q = tid; q < XSZ / 8; q += 256) px[q] = z;
+        for (int q = tid; q < WSZ / 8; q += 256) pw[q] = z;
     };
 
-    const int khalf = lane >> 5;
-    const bool has_tile = wave * 32 < EP;                 // EP = 64: waves 2, 3 idle in the MFMA
-    f32x16 acc[4];
+    // ---- fragments: plane rows are the MFMA's first operand, token rows the
+    // second; slice kk of stage s: x fragment i at fx[kk] + s*XSZ + 32*i*BK,
+    // plane p at fw[kk] + s*WSZ + p*EP*BK --------------------------------------
+    const int kh = lane >> 5, rl = lane & 31;
+    const int et = wave % (EP / 32);                      // expert tile (EP = 64: waves 2, 3 repeat 0, 1)
+    const uint16_t* fx[4];
+    const uint16_t* fw[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int kk = 0; kk < 4; ++kk) {
+        const int ch = kk * 2 + kh;
+        fx[kk] = xs + rl * BK + ((ch ^ rswz(rl)) * 8);
+        fw[kk] = ws + (et * 32 + rl) * BK + ((ch ^ rswz(rl)) * 8);
+    }
+    f32x16 acc[TM];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) acc[i][q] = 0.f;
+    for (int i = 0; i < TM; ++i) acc[i] = f32x16{};
+    bf16x8 tf0[TM], wf0[3], tf1[TM], wf1[3];
 
-    const int nk = H / RV_BK;
-    issue(0);
-    if (1 < nk) issue(1);
-    if (2 < nk) issue(2);
-    for (int kt = 0; kt < nk; ++kt) {
-        const int ahead = nk - 1 - kt;
-        if (ahead >= 2) wait_vmcnt<2 * NI>();
-        else if (ahead == 1) wait_vmcnt<NI>();
-        else wait_vmcnt<0>();
-        block_barrier();
-        if (kt + 3 < nk) issue(kt + 3);
-        if (has_tile) {
-            const uint16_t* st = smem + (kt % RV_STAGES) * STAGE;
+    const int nk = H / BK;
+    const int nkp = (nk + 1) & ~1;                        // even: both steps of an iteration run
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    copies(S0{}, 0, 0, NI);
+    wait_vmcnt<0>();
+    block_barrier();
 #pragma unroll
-            for (int kk = 0; kk < RV_BK / 16; ++kk) {
-                const int ch = kk * 2 + khalf;
-                bf16x8 tf[4], wf[3];
+    for (int i = 0; i < TM; ++i) tf0[i] = *reinterpret_cast<const bf16x8*>(fx[0] + i * 32 * BK);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = i * 32 + (lane & 31);
-                    tf[i] = *reinterpret_cast<const bf16x8*>(st + r * RV_BK + ((ch ^ rswz(r)) * 8));
-                }
+    for (int p = 0; p < 3; ++p) wf0[p] = *reinterpret_cast<const bf16x8*>(fw[0] + p * EP * BK);
+
+    constexpr int NQ = 3 * TM;                            // MFMAs per slice
+    constexpr int NR = TM + 3;                            // fragment reads per slice
+    constexpr int NPRE = NQ - NR;                         // MFMAs of the last slice before the barrier
+    static_assert(NPRE >= 2, "reads fit between the MFMAs");
+    // one slice: MFMAs from (CT, CW), after MFMA Q0 + r the fragment read r of
+    // slice NKK of stage NB into (NT, NW), copies [D0, D1) of k-tile KF spread
+    // over the MFMAs
+#define RV_SLICE(CT, CW, NT_, NW_, NB, NKK, Q0, Q1, TS, KF, DO_COPY, D0, D1)                    \
+    _Pragma("unroll") for (int q = (Q0); q < (Q1); ++q) {                                      \
+        acc[q % TM] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(CW[q / TM], CT[q % TM], acc[q % TM], 0, 0, 0); \
+        const int r_ = q - (Q0);                                                                \
+        if (r_ < TM)                                                                            \
+            NT_[r_] = *reinterpret_cast<const bf16x8*>(fx[NKK] + (NB) * XSZ + r_ * 32 * BK);    \
+        else if (r_ < NR)                                                                       \
+            NW_[r_ - TM] = *reinterpret_cast<const bf16x8*>(fw[NKK] + (NB) * WSZ + (r_ - TM) * EP * BK); \
+        if ((DO_COPY) && (D1) > (D0)) {                                                         \
+            const int per = ((D1) - (D0) + (Q1) - (Q0) - 1) / ((Q1) - (Q0));                    \
+            copies(TS, KF, (D0) + r_ * per, (D0) + r_ * per + per < (D1) ? (D0) + r_ * per + per : (D1)); \
+        }                                                                                       \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+    }
+    // k-tile kt in stage S: slices 0 and 1 carry the copies of k-tile kt + 1
+    // into the other stage (freed by k-tile kt - 1); the last slice brackets
+    // the hand-over (wait, barrier, then reads of slice 0 of k-tile kt + 1)
+    auto step = [&](auto S, int kt) {
+        constexpr int SI = decltype(S)::value;
+        const auto TS = std::integral_constant<int, 1 - SI>{};
+        const int kf = kt + 1;
+        const bool do_copy = kf < nk;
+        if (kf >= nk && kf < nkp) zero_fill(TS);
+        RV_SLICE(tf0, wf0, tf1, wf1, SI, 1, 0, NQ, TS, kf, do_copy, 0, NI / 2)
+        RV_SLICE(tf1, wf1, tf0, wf0, SI, 2, 0, NQ, TS, kf, do_copy, NI / 2, NI)
+        RV_SLICE(tf0, wf0, tf1, wf1, SI, 3, 0, NQ, TS, kf, false, 0, 0)
 #pragma unroll
-                for (int p = 0; p < 3; ++p) {
-                    const int r = RV_TOK + p * EP + wave * 32 + (lane & 31);
-                    wf[p] = *reinterpret_cast<const bf16x8*>(st + r * RV_BK + ((ch ^ rswz(r)) * 8));
-                }
-#pragma unroll
-                for (int p = 0; p < 3; ++p)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[p], tf[i], acc[i], 0, 0, 0);
-            }
+        for (int q = 0; q < NPRE; ++q)
+            acc[q % TM] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf1[q / TM], tf1[q % TM], acc[q % TM], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kf < nkp) {
+            wait_vmcnt<0>();
+            wait_lgkmcnt0();
+            block_barrier();
         }
+        __builtin_amdgcn_sched_barrier(0);
+        RV_SLICE(tf1, wf1, tf0, wf0, 1 - SI, 0, NPRE, NQ, TS, kf, false, 0, 0)
+    };
+#undef RV_SLICE
+    for (int kt = 0; kt < nkp; kt += 2) {
+        step(S0{}, kt);
+        step(S1{}, kt + 1);
     }
 
-    // ---- scores to LDS: lane holds experts 8q + 4*khalf + [0,4) of token (lane&31) ----
+    // ---- scores to LDS: lane holds experts 8q + 4*kh + [0,4) of token rl ----
+    wait_lgkmcnt0();
     block_barrier();
-    float* Cs = reinterpret_cast<float*>(smem);
-    float* Ss = Cs + RV_TOK * PITCH;
-    if (has_tile) {
+    float* Ss = reinterpret_cast<float*>(smem);
+    if (wave < EP / 32) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tok = i * 32 + (lane & 31);
+        for (int i = 0; i < TM; ++i) {
+            const int tok = i * 32 + rl;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int e0 = wave * 32 + 8 * q + 4 * khalf;
-                float cv[4], sv[4];
+                const int e0 = et * 32 + 8 * q + 4 * kh;
+                float sv[4];
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const int e = e0 + p;
-                    const float z = acc[i][4 * q + p];
-                    sv[p] = 1.0f / (1.0f + expf(-z));
-                    cv[p] = e < E ? sv[p] + a.bias[e] : -INFINITY;
-                }
-                *reinterpret_cast<float4*>(Cs + tok * PITCH + e0) = make_float4(cv[0], cv[1], cv[2], cv[3]);
+                for (int p = 0; p < 4; ++p) sv[p] = 1.0f / (1.0f + expf(-acc[i][4 * q + p]));
                 *reinterpret_cast<float4*>(Ss + tok * PITCH + e0) = make_float4(sv[0], sv[1], sv[2], sv[3]);
             }
         }
     }
     __syncthreads();
 
-    // ---- selection: lane-per-token (lanes 0-31 of every wave) -------------------
-    if (lane >= 32) return;
-    const int tok = wave * 32 + lane;
+    // ---- selection: lane-per-token, c = s + bias ------------------------------
+    const int tok = tid;
+    if (tok >= TOK) return;
     const int64_t t = t0 + tok;
     if (t >= a.T) return;
-    const float* crow = Cs + tok * PITCH;
+    const float* srow = Ss + tok * PITCH;
     const int G = a.G, NG = a.NG;
 
     // in-group top-2 sums
@@ -462,8 +520,9 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(RouteV2Args a) {
         if (j < NG) {
             float b1 = -INFINITY, b2 = -INFINITY;
             for (int e = j * G; e < (j + 1) * G; e += 4) {
-                const float4 v4 = *reinterpret_cast<const float4*>(crow + e);
-                const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+                const float4 v4 = *reinterpret_cast<const float4*>(srow + e);
+                const float4 b4 = *reinterpret_cast<const float4*>(s_bias + e);
+                const float vv[4] = {v4.x + b4.x, v4.y + b4.y, v4.z + b4.z, v4.w + b4.w};
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const float v = vv[u];
@@ -494,8 +553,9 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(RouteV2Args a) {
         const int j = __builtin_ctz(rem);
         rem &= rem - 1;
         for (int e = j * G; e < (j + 1) * G; e += 4) {
-            const float4 v4 = *reinterpret_cast<const float4*>(crow + e);
-            const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+            const float4 v4 = *reinterpret_cast<const float4*>(srow + e);
+            const float4 b4 = *reinterpret_cast<const float4*>(s_bias + e);
+            const float vv[4] = {v4.x + b4.x, v4.y + b4.y, v4.z + b4.z, v4.w + b4.w};
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const float c = vv[u];
@@ -514,7 +574,6 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(RouteV2Args a) {
         }
     }
     // weights from the raw scores, slot order sum, scaled once
-    const float* srow = Ss + tok * PITCH;
     const bool valid = a.mask == nullptr || a.mask[t] != 0;
     float sk[KMAX];
     float sum = 0.f;
@@ -573,14 +632,27 @@ hipError_t launch_route(const Dims& d, const void* x, const float* router_w, con
         a.G = d.G;
         a.norm = d.norm;
         a.rsf = d.rsf;
-        const dim3 grid(static_cast<unsigned>((d.T + RV_TOK - 1) / RV_TOK));
-        if (d.E <= 64) {
-            if (d.K <= 8) hipLaunchKernelGGL((route_bf16_kernel<64, 8>), grid, dim3(256), 0, stream, a);
-            else hipLaunchKernelGGL((route_bf16_kernel<64, 16>), grid, dim3(256), 0, stream, a);
-        } else {
-            if (d.K <= 8) hipLaunchKernelGGL((route_bf16_kernel<128, 8>), grid, dim3(256), 0, stream, a);
-            else hipLaunchKernelGGL((route_bf16_kernel<128, 16>), grid, dim3(256), 0, stream, a);
+        // tokens per workgroup: the fewest (32 TM, TM = 4..6) whose grid fits
+        // in one round over the CUs, else the most
+        const int ncu = cu_count();
+        int tm = 6;
+        for (int c = 4; c <= 6; ++c) {
+            if ((d.T + 32 * c - 1) / (32 * c) <= ncu) { tm = c; break; }
         }
+        const dim3 grid(static_cast<unsigned>((d.T + 32 * tm - 1) / (32 * tm)));
+#define RV_LAUNCH(TM_, EP_, KM_) \
+        hipLaunchKernelGGL((route_bf16_kernel<TM_, EP_, KM_>), grid, dim3(256), 0, stream, a)
+#define RV_BY_TM(EP_, KM_)                    \
+        if (tm == 4) RV_LAUNCH(4, EP_, KM_);  \
+        else if (tm == 5) RV_LAUNCH(5, EP_, KM_); \
+        else RV_LAUNCH(6, EP_, KM_);
+        if (d.E <= 64) {
+            if (d.K <= 8) { RV_BY_TM(64, 8) } else { RV_BY_TM(64, 16) }
+        } else {
+            if (d.K <= 8) { RV_BY_TM(128, 8) } else { RV_BY_TM(128, 16) }
+        }
+#undef RV_BY_TM
+#undef RV_LAUNCH
         return hipGetLastError();
     }
     RouteArgs a;
