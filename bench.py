@@ -39,6 +39,9 @@ def parse():
     p.add_argument("--cpu-sample", type=int, default=8192,
                    help="tokens of the same workload the CPU oracle is timed on")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="after the measurements, run a plain 1 GiB device copy three times, so "
+                        "that a hardware-counter run can scale its byte counters")
     return p.parse_args()
 
 
@@ -202,6 +205,13 @@ def main():
                                "sample": "%d of %d tokens of %s, evenly spaced; %.1f s" %
                                          (n, T, wl.name, dt)}
     print(json.dumps(res), flush=True)
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 29, dtype=torch.float16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
 
 if __name__ == "__main__":

@@ -244,7 +244,7 @@ lbv_status lbv_moe_gemm_w2_combine(const lbv_moe_config* cfg, int64_t T, const v
         !aligned4(topk_w))
         return LBV_ERR_ALIGN;
     if (ws_bytes < w2_ws_bytes(d)) return LBV_ERR_WORKSPACE;
-    hipError_t e = lbv::launch_gemm_w2(d, act, w2, shared_w2, offsets, ws, stream);
+    hipError_t e = lbv::launch_gemm_w2(d, act, w2, shared_w2, offsets, sorted_rows, ws, stream);
     if (e != hipSuccess) return LBV_ERR_HIP;
     return hip_status(lbv::launch_combine(d, ws, inv_rows, topk_w, out, stream));
 }
@@ -283,7 +283,7 @@ lbv_status lbv_moe_forward(const lbv_moe_config* cfg, int64_t T, const void* x,
     hipError_t e = lbv::launch_route(d, x, router_w, e_bias, mask, ids, w, rws, stream);
     if (e == hipSuccess) e = lbv::launch_permute(d, ids, offsets, sorted, inv, perm, stream);
     if (e == hipSuccess) e = lbv::launch_gemm_w13(d, x, w13, shared_w13, offsets, sorted, act, stream);
-    if (e == hipSuccess) e = lbv::launch_gemm_w2(d, act, w2, shared_w2, offsets, y, stream);
+    if (e == hipSuccess) e = lbv::launch_gemm_w2(d, act, w2, shared_w2, offsets, sorted, y, stream);
     if (e == hipSuccess) e = lbv::launch_combine(d, y, inv, w, out, stream);
     return hip_status(e);
 }

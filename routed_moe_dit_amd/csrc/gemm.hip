@@ -8,8 +8,8 @@
 // article, "MoE 实现的源码级要点": grouped bf16 matmuls over expert-sorted
 // token copies, fp32 weighted restore):
 //   gate/up:  act[r] = silu(W_gate x[t]) * (W_up x[t])   per sorted row r
-//   down:     y[r]   = W2 act[r]
-//   combine:  out[t] = sum_k w[t,k] y[inv(t,k)] + sum_j y[inv(t,K+j)]
+//   down:     y[slot(r)] = W2 act[r]   (stored back in slot order t*KS + k)
+//   combine:  out[t] = sum_k w[t,k] y[t*KS+k] + sum_j y[t*KS+K+j]   (routed slots only)
 //
 // Segments s < E are routed experts, s >= E shared pseudo-experts (a width
 // I slice of the shared MLP, exact by linearity of the down projection).
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     constexpr int ASZ = BM * BK, BSZ = BN * BK;  // bf16 elements of one stage's A / B part
     __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * STAGE];
     __shared__ int s_pre[kMaxSeg + 1];           // m-tiles before segment s
-    __shared__ int s_rid[4][64];                 // next tile's slot ids, per wave
+    __shared__ int s_rid[4][64];                 // slot ids: gate/up: next tile's, per wave; down: this tile's
     __shared__ int s_tmp[8];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -234,8 +234,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     const uint16_t* abase;
     const uint16_t* bbase;
     uint32_t aoff[AI], boff[BI];
-    // Slot ids of this wave's 64 A rows of a tile, copied into s_rid[wave]
-    // (gate/up only; a copy like the stage copies, counted by the same waits).
+    // Slot ids of this wave's 64 A rows of a tile, copied into s_rid[wave] (a
+    // copy like the stage copies, counted by the same waits).  The gate/up
+    // matmul gathers its x rows by them; the down matmul stores its output
+    // rows to them.
     auto rid_copy = [&](int seg_r0_, int seg_n_, int m0_) {
         int m = m0_ + wave * 64 + lane;
         if (m >= seg_n_) m = seg_n_ - 1;
@@ -438,6 +440,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
         const int kc = last ? 0 : kf;            // k-tile index of the copies
         if (kf >= nk && !last) zero_fill(TS);
         if (MODE == 0 && kt == 0 && has_next) rid_copy(nseg_r0, nseg_n, nm0);
+        if (MODE == 1 && kt == 0) rid_copy(seg_r0, seg_n, m0);
 #pragma unroll
         for (int kk = 0; kk < KKS - 1; ++kk) {
             if (kk % 2 == 0) {
@@ -550,8 +553,11 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
                 const int m = m0 + wm * (BM / 2) + p * PROWS + row;
                 const int col = col0 + ch * 8;
                 const u32x4 v = *reinterpret_cast<const u32x4*>(ep + ep_off(row, ch * 8));
+                // gate/up: act rows in segment order; down: y rows in slot order
+                const int64_t orow = MODE == 0 ? seg_r0 + m
+                                               : (&s_rid[0][0])[wm * (BM / 2) + p * PROWS + row];
                 if (m < seg_n && col < ncols)
-                    *reinterpret_cast<u32x4*>(C + static_cast<int64_t>(seg_r0 + m) * ncols + col) = v;
+                    *reinterpret_cast<u32x4*>(C + orow * ncols + col) = v;
             }
         }
         if (!has_next) break;
@@ -666,16 +672,20 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
             if (m < seg_n && n < a.ncols) {
                 float v = accg[i][j];
                 if (MODE == 0) v = v * accu[i][j] / (1.0f + expf(-v));
-                C[static_cast<int64_t>(seg_r0 + m) * a.ncols + n] = v;
+                // gate/up: act rows in segment order; down: y rows in slot order
+                const int64_t orow = MODE == 0 ? seg_r0 + m : a.rows[seg_r0 + m];
+                C[orow * a.ncols + n] = v;
             }
         }
 }
 
 // ---------------------------------------------------------------------------
-// Combine: one wave per token; per step a lane owns 16 contiguous bytes of the
-// output row and first issues the loads of all the token's slot rows at once
-// (the step is bound by HBM latency and bandwidth), then sums them in slot
-// order in fp32 and rounds once.
+// Combine: one wave per token; the token's slot rows t*KS .. t*KS+KS-1 of y
+// are contiguous (the down matmul stores them in slot order), so the step
+// streams them.  Per step a lane owns 16 contiguous bytes of the output row
+// and first issues the loads of all the token's routed slot rows, then sums
+// them in slot order in fp32 and rounds once.  inv_rows only marks the empty
+// slots (-1) of padding tokens.
 // ---------------------------------------------------------------------------
 struct CombArgs {
     const void* y;
@@ -701,7 +711,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
         rows[k] = -1;
         wt[k] = 1.0f;
         if (k < a.KS) {
-            rows[k] = a.inv[t * a.KS + k];
+            rows[k] = a.inv[t * a.KS + k] < 0 ? -1 : static_cast<int>(t * a.KS + k);
             if (k < a.K) wt[k] = a.w[t * a.K + k];
         }
     }
@@ -748,7 +758,7 @@ constexpr int G1_BM = LBV_G1_BM, G1_BN = LBV_G1_BN;
 constexpr int G2_BM = LBV_G2_BM, G2_BN = LBV_G2_BN;
 
 GemmArgs make_args(const Dims& d) {
-    GemmArgs a;
+    GemmArgs a{};
     a.T = d.T;
     a.H = d.H;
     a.I = d.I;
@@ -791,13 +801,14 @@ hipError_t launch_gemm_w13(const Dims& d, const void* x, const void* w13,
 }
 
 hipError_t launch_gemm_w2(const Dims& d, const void* act, const void* w2, const void* shared_w2,
-                          const int32_t* offsets, void* y, hipStream_t stream) {
+                          const int32_t* offsets, const int32_t* sorted_rows, void* y,
+                          hipStream_t stream) {
     GemmArgs a = make_args(d);
     a.A = act;
     a.B = w2;
     a.Bsh = shared_w2;
     a.offsets = offsets;
-    a.rows = nullptr;
+    a.rows = sorted_rows;                        // slot of each sorted row: y is stored in slot order
     a.C = y;
     a.kdim = d.I;
     a.ncols = d.H;

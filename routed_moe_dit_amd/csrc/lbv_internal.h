@@ -63,7 +63,8 @@ hipError_t launch_gemm_w13(const Dims& d, const void* x, const void* w13,
                            const int32_t* sorted_rows, void* act, hipStream_t stream);
 
 hipError_t launch_gemm_w2(const Dims& d, const void* act, const void* w2, const void* shared_w2,
-                          const int32_t* offsets, void* y, hipStream_t stream);
+                          const int32_t* offsets, const int32_t* sorted_rows, void* y,
+                          hipStream_t stream);
 
 hipError_t launch_combine(const Dims& d, const void* y, const int32_t* inv_rows,
                           const float* topk_w, void* out, hipStream_t stream);
