@@ -24,10 +24,13 @@ sys.path.insert(0, ROOT)
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0
 
-# HBM bytes of the gate/up GEMM per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE
-# on default_gen_T38000, scaled by the counter-to-bytes factor of a plain copy
-# kernel (None until measured for the current kernel).
-GEMM_W13_TRAFFIC_BYTES = None
+# Bytes the gate/up GEMM moves between L2 and memory per launch on
+# default_gen_T38000: rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch,
+# two --pmc runs of `bench.py --copy-calibration`), each scaled by what the same
+# counter reads for a plain 1 GiB device copy (FETCH_SIZE x 2.000, WRITE_SIZE
+# x 1.000): 3,316,368 KiB x 2 read + 621,276 KiB written.  Re-measure whenever
+# the kernel changes (None then).
+GEMM_W13_TRAFFIC_BYTES = 7.4279e9
 
 
 def parse():
