@@ -14,23 +14,23 @@
 // Segments s < E are routed experts, s >= E shared pseudo-experts (a width
 // I slice of the shared MLP, exact by linearity of the down projection).
 //
-// bf16 path: one workgroup (4 waves, 256 threads) computes a BM x BN tile of
-// one segment with v_mfma_f32_32x32x16_bf16 (2 x 2 waves of 128 x 128).  A and
-// B tiles (K-contiguous, BK = 64 bf16 = 128 B per row, so every copy
-// instruction moves whole 128-byte lines) go straight from global memory to
-// LDS with global_load_lds_dwordx4 into a ring of STAGES k-tiles.  The copies
-// of the next k-tile are spread one by one between the MFMAs of the current
-// one (a burst of copies stalls the issuing wave, and with one wave per SIMD
-// that idles the matrix core); the LDS reads of slice g + 1 likewise sit
-// between the MFMAs of slice g; one barrier per k-tile hands a stage over.
-// LDS rows are 16-byte chunks, chunk c of row r stored at c ^ ((r >> 1) & 7),
-// which makes the fragment reads conflict-free.  Tiles never cross a
-// segment: the tile list is rebuilt from `offsets` by every workgroup (no
-// host read-back of segment sizes), and the grid is sized for the worst case;
-// surplus workgroups exit at once.  For the gate/up matmul a B tile holds
-// BN/2 gate rows and the matching BN/2 up rows, and each wave's accumulators
-// for gate column n and up column n sit in the same lane and register, so
-// silu(g) * u is formed in registers.
+// bf16 path: a persistent workgroup per CU computes 256 x 256 tiles of one
+// segment at a time with v_mfma_f32_32x32x16_bf16: 8 waves in 2 x 4, each
+// with 128 x 64 fp32 accumulators, two waves per SIMD so that one can issue
+// MFMAs while the other waits.  A and B tiles (K-contiguous, BK = 64 bf16 =
+// 128 B per row, so every copy instruction moves whole 128-byte lines) go
+// straight from global memory to LDS with global_load_lds_dwordx4 into two
+// stages.  Waves 0-3 (one per SIMD) issue the copies of the next k-tile one
+// at a time between their MFMAs of the current one (a burst of copies stalls
+// the issuing wave until the address unit takes them); the LDS reads of
+// slice g + 1 sit between the MFMAs of slice g; one barrier per k-tile hands a
+// stage over.  LDS rows are 16-byte chunks, chunk c of row r stored at
+// c ^ ((r >> 1) & 7), which makes the fragment reads conflict-free.  Tiles
+// never cross a segment; the tile table is built on the device from
+// `offsets` (no host read-back of segment sizes).  For the gate/up matmul a B
+// tile holds BN/2 gate rows and the matching BN/2 up rows, and each wave's
+// accumulators for gate column n and up column n sit in the same lane and
+// register, so silu(g) * u is formed in registers.
 #include <type_traits>
 
 #include "lbv_internal.h"
@@ -39,12 +39,23 @@
 // Compile-time shape of the bf16 path: workgroup tile BM x BN (2 x 2 waves;
 // the gate/up GEMM's BN counts gate and up rows together, BN/2 act columns
 // per tile); NPRE: MFMAs of a k-tile's last slice issued before its barrier;
-// COPY_SLICES: slices of a k-tile that carry the next k-tile's copies.
+// COPY_SLICES: slices of a k-tile that carry the next k-tile's copies;
+// G*_WAVES: waves per workgroup (4 or 8); COPY_WAVES: waves that issue the
+// stage copies.
 #ifndef LBV_NPRE
 #define LBV_NPRE 8
 #endif
 #ifndef LBV_COPY_SLICES
 #define LBV_COPY_SLICES 2
+#endif
+#ifndef LBV_COPY_WAVES
+#define LBV_COPY_WAVES 4
+#endif
+#ifndef LBV_G1_WAVES
+#define LBV_G1_WAVES 8
+#endif
+#ifndef LBV_G2_WAVES
+#define LBV_G2_WAVES 8
 #endif
 #ifndef LBV_G1_BM
 #define LBV_G1_BM 256
@@ -148,19 +159,27 @@ constexpr int kMaxSeg = 512;
 // one continuous k-loop over all its tiles: the copies of the next tile's
 // first k-tile are issued during the current tile's last k-tile and land
 // while its epilogue runs.
-template <int BM, int BN, int MODE>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
+template <int BM, int BN, int MODE, int NW>
+__global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
+    // NW waves: 2 along the tokens x NW/2 along the weight rows (NW = 4: one
+    // wave per SIMD with 128 x 128 accumulators; NW = 8: two per SIMD with
+    // 128 x 64, so that one wave's MFMAs can cover the other's waits).
+    constexpr int NTH = NW * 64;
+    constexpr int WN = NW / 2;
     constexpr int BK = 64;                       // bf16 per row per k-tile: 128 bytes
     constexpr int TM = BM / 64;                  // token tiles (32 rows) per wave
-    constexpr int TN = BN / 64;                  // weight-row tiles (32 rows) per wave
+    constexpr int TN = BN / WN / 32;             // weight-row tiles (32 rows) per wave
     static_assert(MODE == 1 || TN % 2 == 0, "gate/up tiles come in pairs");
     constexpr int STAGE = (BM + BN) * BK;        // bf16 elements per stage
     constexpr int CPR = BK / 8;                  // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;                // rows per 1 KB copy instruction
-    constexpr int AI = BM / 4 / RPI, BI = BN / 4 / RPI;  // copies per wave per k-tile
+    // Waves 0 .. CW-1 issue the stage copies (with NW = 8 and CW = 4 one wave
+    // per SIMD copies while the other only multiplies).
+    constexpr int CW = LBV_COPY_WAVES < NW ? LBV_COPY_WAVES : NW;
+    constexpr int AI = BM / CW / RPI, BI = BN / CW / RPI;  // copies per copying wave per k-tile
     constexpr int NI = AI + BI;
     constexpr int KKS = BK / 16;                 // 16-deep k-slices per k-tile
-    static_assert(BM / 4 == 64, "one row-id copy (64 rows) per wave");
+    static_assert(BM == 256 && BN == BM, "slot ids: 4 waves x 64 rows; staging split evenly");
 
     // Two stages laid out [A0 | A1 | B0 | B1] (A: token rows, B: weight rows),
     // so that a fragment read is one base register per slice plus an
@@ -169,43 +188,47 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     constexpr int ASZ = BM * BK, BSZ = BN * BK;  // bf16 elements of one stage's A / B part
     __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * STAGE];
     __shared__ int s_pre[kMaxSeg + 1];           // m-tiles before segment s
-    __shared__ int s_rid[4][64];                 // slot ids: gate/up: next tile's, per wave; down: this tile's
+    __shared__ int s_rid[BM];                    // slot ids of a tile's rows: gate/up: the next tile's; down: this tile's
     __shared__ int s_tmp[8];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
     const int khalf = lane >> 5;
     const int Is = a.NS * a.I;
 
     // ---- segment tile table: s_pre[s] = sum over s' < s of ceil(n_s' / BM) ----
     {
-        int c[2], inc[2];
+        // threads 0..255 (waves 0..3) scan two values each
+        int c[2] = {0, 0}, inc[2] = {0, 0};
+        if (wave < 4) {
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int s = tid + p * 256;
-            c[p] = 0;
-            if (s < a.S) {
-                const int n = a.offsets[s + 1] - a.offsets[s];
-                c[p] = n > 0 ? (n + BM - 1) / BM : 0;
-            }
-            int v = c[p];
+            for (int p = 0; p < 2; ++p) {
+                const int s = tid + p * 256;
+                if (s < a.S) {
+                    const int n = a.offsets[s + 1] - a.offsets[s];
+                    c[p] = n > 0 ? (n + BM - 1) / BM : 0;
+                }
+                int v = c[p];
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int o = __shfl_up(v, off);
-                if (lane >= off) v += o;
+                for (int off = 1; off < 64; off <<= 1) {
+                    const int o = __shfl_up(v, off);
+                    if (lane >= off) v += o;
+                }
+                inc[p] = v;
+                if (lane == 63) s_tmp[p * 4 + wave] = v;
             }
-            inc[p] = v;
-            if (lane == 63) s_tmp[p * 4 + wave] = v;
         }
         __syncthreads();
-        int base0 = 0, base1 = s_tmp[0] + s_tmp[1] + s_tmp[2] + s_tmp[3];
-        for (int w = 0; w < wave; ++w) {
-            base0 += s_tmp[w];
-            base1 += s_tmp[4 + w];
+        if (wave < 4) {
+            int base0 = 0, base1 = s_tmp[0] + s_tmp[1] + s_tmp[2] + s_tmp[3];
+            for (int w = 0; w < wave; ++w) {
+                base0 += s_tmp[w];
+                base1 += s_tmp[4 + w];
+            }
+            if (tid < a.S) s_pre[tid + 1] = base0 + inc[0];
+            if (tid + 256 < a.S) s_pre[tid + 257] = base1 + inc[1];
         }
-        if (tid < a.S) s_pre[tid + 1] = base0 + inc[0];
-        if (tid + 256 < a.S) s_pre[tid + 257] = base1 + inc[1];
         if (tid == 0) s_pre[0] = 0;
         __syncthreads();
     }
@@ -234,18 +257,21 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     const uint16_t* abase;
     const uint16_t* bbase;
     uint32_t aoff[AI], boff[BI];
-    // Slot ids of this wave's 64 A rows of a tile, copied into s_rid[wave] (a
-    // copy like the stage copies, counted by the same waits).  The gate/up
-    // matmul gathers its x rows by them; the down matmul stores its output
-    // rows to them.
+    // Slot ids of a tile's BM rows, copied into s_rid by waves 0..3, 64 rows
+    // each (a copy like the stage copies, counted by the same waits).  The
+    // gate/up matmul gathers its x rows by them; the down matmul stores its
+    // output rows to them.
     auto rid_copy = [&](int seg_r0_, int seg_n_, int m0_) {
-        int m = m0_ + wave * 64 + lane;
-        if (m >= seg_n_) m = seg_n_ - 1;
-        lds_dma4_sb(a.rows, static_cast<uint32_t>(seg_r0_ + m) * 4, lds_addr(&s_rid[wave][0]));
+        if (wave < 4) {
+            int m = m0_ + wave * 64 + lane;
+            if (m >= seg_n_) m = seg_n_ - 1;
+            lds_dma4_sb(a.rows, static_cast<uint32_t>(seg_r0_ + m) * 4, lds_addr(&s_rid[wave * 64]));
+        }
     };
     // Points the copy sources at tile (seg_, m0_, nt_); gate/up reads the slot
-    // ids from s_rid[wave], which must have landed.
+    // ids from s_rid, which must have landed (and be visible: a barrier).
     auto set_sources = [&](int seg_, int seg_r0_, int seg_n_, int m0_, int nt_) {
+        if (CW < NW && wave >= CW) return;       // not a copying wave
         // lane-derived terms are recomputed here rather than hoisted out of
         // the tile loop (where they would hold registers through the k-loop)
         const int lane = (threadIdx.x & 63) + opaque_zero();
@@ -262,10 +288,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < AI; ++i) {
-            const int r = wave * (BM / 4) + i * RPI + lane / CPR;
+            const int r = wave * (BM / CW) + i * RPI + lane / CPR;
             const uint32_t c = (lane % CPR) ^ swz<BK>(r);
             if (MODE == 0) {
-                int tok = s_rid[wave][i * RPI + lane / CPR] / a.KS;
+                int tok = s_rid[r] / a.KS;
                 tok = tok < 0 ? 0 : (tok >= a.T ? static_cast<int>(a.T) - 1 : tok);
                 aoff[i] = (__umul24(tok, a.H) + c * 8) * 2;
             } else {
@@ -276,7 +302,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < BI; ++i) {
-            const int r = wave * (BN / 4) + i * RPI + lane / CPR;
+            const int r = wave * (BN / CW) + i * RPI + lane / CPR;
             const uint32_t c = (lane % CPR) ^ swz<BK>(r);
             if (MODE == 0) {
                 const int half = r / (BN / 2);
@@ -293,8 +319,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
         }
     };
 
-    const int a_lds = wave * (BM / 4) * BK;      // this wave's rows inside an A / B part
-    const int b_lds = wave * (BN / 4) * BK;
+    const int a_lds = wave * (BM / CW) * BK;     // this wave's rows inside an A / B part
+    const int b_lds = wave * (BN / CW) * BK;
     const int nk = a.kdim / BK;
     // the k-loop of a tile runs over nkp = nk rounded up to even, so that both
     // steps of an iteration are unconditional (no MFMA under a branch); the
@@ -308,13 +334,14 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
         u32x4* pb = reinterpret_cast<u32x4*>(b_part(S));
         const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int q = 0; q < ASZ / 8 / 256; ++q) pa[tid + 256 * q] = z;
+        for (int q = 0; q < ASZ / 8 / NTH; ++q) pa[tid + NTH * q] = z;
 #pragma unroll
-        for (int q = 0; q < BSZ / 8 / 256; ++q) pb[tid + 256 * q] = z;
+        for (int q = 0; q < BSZ / 8 / NTH; ++q) pb[tid + NTH * q] = z;
     };
     // copy instruction D (A rows first, then B rows) of k-tile kt into stage S
     auto copy_const = [&](auto S, int kt, auto D) {
         constexpr int d = decltype(D)::value;
+        if (CW < NW && wave >= CW) return;
         if constexpr (d < AI)
             lds_dma16_sb<d * RPI * BK * 2>(abase + kt * BK, aoff[d], lds_addr(a_part(S) + a_lds));
         else
@@ -340,7 +367,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
         const int ln = (threadIdx.x & 63) + opaque_zero();
         const int kh = ln >> 5, rl = ln & 31;
         const int ra = wm * (BM / 2) + rl;                       // first A row (i = 0)
-        const int rb = (MODE == 0 ? wn * (BN / 4) : wn * (BN / 2)) + rl;   // first B row (j = 0)
+        const int rb = (MODE == 0 ? wn * (BN / 2 / WN) : wn * (BN / WN)) + rl;   // first B row (j = 0)
 #pragma unroll
         for (int kk = 0; kk < KKS; ++kk) {
             const int ch = kk * 2 + kh;                          // swz(r) depends on r mod 32 only
@@ -371,6 +398,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     if (MODE == 0) {
         rid_copy(seg_r0, seg_n, m0);
         wait_vmcnt<0>();
+        block_barrier();
     }
     set_sources(seg, seg_r0, seg_n, m0, nt);
 #pragma unroll
@@ -383,8 +411,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     for (int j = 0; j < TN; ++j) wf0[j] = *reinterpret_cast<const bf16x8*>(fb[0] + brow(j) * BK);
 
     constexpr int NQ = TM * TN;                  // MFMAs per slice
-    constexpr int NPRE = LBV_NPRE;               // MFMAs of the last slice before the barrier
     constexpr int NR = TM + TN;                  // fragment reads per slice
+    constexpr int NPRE = LBV_NPRE < NQ - NR ? LBV_NPRE : NQ - NR;   // MFMAs of the last slice before the barrier
     static_assert(NQ >= NR + NPRE, "reads fit between the MFMAs");
     constexpr int DSL = LBV_COPY_SLICES < KKS - 1 ? LBV_COPY_SLICES : KKS - 1;   // slices carrying copies
 
@@ -471,12 +499,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     };
 #undef LBV_SLICE
 
-    constexpr int WCOLS = MODE == 0 ? BN / 4 : BN / 2;   // output columns per wave
+    constexpr int WCOLS = MODE == 0 ? BN / 2 / WN : BN / WN;   // output columns per wave
     constexpr int CHUNKS = WCOLS / 8;                    // 16-byte chunks per row
-    constexpr int PROWS = 8192 / WCOLS;                  // rows per staging pass (16 KB per wave)
+    constexpr int RSZ = 2 * ASZ / NW;                    // staging elements per wave (stage 1 split evenly)
+    constexpr int PROWS = RSZ / WCOLS;                   // rows per staging pass
     constexpr int PT = PROWS / 32;                       // token tiles per pass
-    static_assert(2 * 8192 <= ASZ && 2 * 8192 <= BSZ, "staging fits in stage 1");
-    uint16_t* const ep0 = (wave < 2 ? lds + ASZ : lds + 2 * ASZ + BSZ) + (wave & 1) * 8192;   // this wave's staging region
+    static_assert(PT >= 1 && TM % PT == 0, "whole token tiles per pass");
+    uint16_t* const ep0 = (wave < NW / 2 ? lds + ASZ : lds + 2 * ASZ + BSZ) + (wave % (NW / 2)) * RSZ;   // this wave's staging region
     auto ep_off = [&](int row, int col) {                // element offset of (row, col) in the region
         return row * WCOLS + (((col >> 3) ^ (row % CHUNKS)) << 3) + (col & 7);
     };
@@ -507,7 +536,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
         // reads them back 16 bytes per lane, so that every global store
         // instruction writes whole contiguous rows.  Every wave passed the last
         // barrier after its final reads of stage 1.
-        const int col0 = MODE == 0 ? nt * (BN / 2) + wn * (BN / 4) : nt * BN + wn * (BN / 2);
+        const int col0 = MODE == 0 ? nt * (BN / 2) + wn * (BN / 2 / WN) : nt * BN + wn * (BN / WN);
         // staging addresses are formed here, not hoisted out of the tile loop
         // (where they would hold registers through the whole k-loop)
         uint16_t* const ep = ep0;
@@ -554,8 +583,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
                 const int col = col0 + ch * 8;
                 const u32x4 v = *reinterpret_cast<const u32x4*>(ep + ep_off(row, ch * 8));
                 // gate/up: act rows in segment order; down: y rows in slot order
-                const int64_t orow = MODE == 0 ? seg_r0 + m
-                                               : (&s_rid[0][0])[wm * (BM / 2) + p * PROWS + row];
+                const int64_t orow = MODE == 0 ? seg_r0 + m : s_rid[wm * (BM / 2) + p * PROWS + row];
                 if (m < seg_n && col < ncols)
                     *reinterpret_cast<u32x4*>(C + orow * ncols + col) = v;
             }
@@ -789,8 +817,8 @@ hipError_t launch_gemm_w13(const Dims& d, const void* x, const void* w13,
     a.ncols = d.I;
     if (d.bf16) {
         a.ntn = (d.I + G1_BN / 2 - 1) / (G1_BN / 2);
-        hipLaunchKernelGGL((gemm_bf16_kernel<G1_BM, G1_BN, 0>), dim3(cu_count() / 8 * 8), dim3(256),
-                           0, stream, a);
+        hipLaunchKernelGGL((gemm_bf16_kernel<G1_BM, G1_BN, 0, LBV_G1_WAVES>), dim3(cu_count() / 8 * 8),
+                           dim3(LBV_G1_WAVES * 64), 0, stream, a);
     } else {
         a.ntn = (d.I + 31) / 32;
         const int64_t grid = max_mtiles(d, 32) * a.ntn;
@@ -814,8 +842,8 @@ hipError_t launch_gemm_w2(const Dims& d, const void* act, const void* w2, const 
     a.ncols = d.H;
     if (d.bf16) {
         a.ntn = (d.H + G2_BN - 1) / G2_BN;
-        hipLaunchKernelGGL((gemm_bf16_kernel<G2_BM, G2_BN, 1>), dim3(cu_count() / 8 * 8), dim3(256),
-                           0, stream, a);
+        hipLaunchKernelGGL((gemm_bf16_kernel<G2_BM, G2_BN, 1, LBV_G2_WAVES>), dim3(cu_count() / 8 * 8),
+                           dim3(LBV_G2_WAVES * 64), 0, stream, a);
     } else {
         a.ntn = (d.H + 31) / 32;
         const int64_t grid = max_mtiles(d, 32) * a.ntn;
