@@ -40,16 +40,19 @@
 // the gate/up GEMM's BN counts gate and up rows together, BN/2 act columns
 // per tile); NPRE: MFMAs of a k-tile's last slice issued before its barrier;
 // COPY_SLICES: slices of a k-tile that carry the next k-tile's copies;
-// G*_WAVES: waves per workgroup (4 or 8); COPY_WAVES: waves that issue the
-// stage copies.
+// G*_WAVES: waves per workgroup (4 or 8); G*_COPY_WAVES: waves that issue
+// the stage copies.
 #ifndef LBV_NPRE
 #define LBV_NPRE 8
 #endif
 #ifndef LBV_COPY_SLICES
 #define LBV_COPY_SLICES 2
 #endif
-#ifndef LBV_COPY_WAVES
-#define LBV_COPY_WAVES 4
+#ifndef LBV_G1_COPY_WAVES
+#define LBV_G1_COPY_WAVES 4
+#endif
+#ifndef LBV_G2_COPY_WAVES
+#define LBV_G2_COPY_WAVES 4
 #endif
 #ifndef LBV_G1_WAVES
 #define LBV_G1_WAVES 8
@@ -159,7 +162,7 @@ constexpr int kMaxSeg = 512;
 // one continuous k-loop over all its tiles: the copies of the next tile's
 // first k-tile are issued during the current tile's last k-tile and land
 // while its epilogue runs.
-template <int BM, int BN, int MODE, int NW>
+template <int BM, int BN, int MODE, int NW, int CWV>
 __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     // NW waves: 2 along the tokens x NW/2 along the weight rows (NW = 4: one
     // wave per SIMD with 128 x 128 accumulators; NW = 8: two per SIMD with
@@ -175,7 +178,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     constexpr int RPI = 64 / CPR;                // rows per 1 KB copy instruction
     // Waves 0 .. CW-1 issue the stage copies (with NW = 8 and CW = 4 one wave
     // per SIMD copies while the other only multiplies).
-    constexpr int CW = LBV_COPY_WAVES < NW ? LBV_COPY_WAVES : NW;
+    constexpr int CW = CWV < NW ? CWV : NW;
     constexpr int AI = BM / CW / RPI, BI = BN / CW / RPI;  // copies per copying wave per k-tile
     constexpr int NI = AI + BI;
     constexpr int KKS = BK / 16;                 // 16-deep k-slices per k-tile
@@ -817,7 +820,7 @@ hipError_t launch_gemm_w13(const Dims& d, const void* x, const void* w13,
     a.ncols = d.I;
     if (d.bf16) {
         a.ntn = (d.I + G1_BN / 2 - 1) / (G1_BN / 2);
-        hipLaunchKernelGGL((gemm_bf16_kernel<G1_BM, G1_BN, 0, LBV_G1_WAVES>), dim3(cu_count() / 8 * 8),
+        hipLaunchKernelGGL((gemm_bf16_kernel<G1_BM, G1_BN, 0, LBV_G1_WAVES, LBV_G1_COPY_WAVES>), dim3(cu_count() / 8 * 8),
                            dim3(LBV_G1_WAVES * 64), 0, stream, a);
     } else {
         a.ntn = (d.I + 31) / 32;
@@ -842,7 +845,7 @@ hipError_t launch_gemm_w2(const Dims& d, const void* act, const void* w2, const 
     a.ncols = d.H;
     if (d.bf16) {
         a.ntn = (d.H + G2_BN - 1) / G2_BN;
-        hipLaunchKernelGGL((gemm_bf16_kernel<G2_BM, G2_BN, 1, LBV_G2_WAVES>), dim3(cu_count() / 8 * 8),
+        hipLaunchKernelGGL((gemm_bf16_kernel<G2_BM, G2_BN, 1, LBV_G2_WAVES, LBV_G2_COPY_WAVES>), dim3(cu_count() / 8 * 8),
                            dim3(LBV_G2_WAVES * 64), 0, stream, a);
     } else {
         a.ntn = (d.H + 31) / 32;

@@ -102,6 +102,12 @@ def test_bf16_offset_limits():
     big = dict(hidden=1 << 15, intermediate=1 << 15)     # w13 of one expert: 4 GiB in bf16
     assert lbv.lbv_moe_check_config(lbv.config(**big)) == lbv.LBV_ERR_SHAPE
     assert lbv.lbv_moe_check_config(lbv.config(dtype="f32", **big)) == lbv.LBV_OK
+    # row offsets are formed with 24-bit multiplies: T, hidden and gate/up rows below 2^24
+    small_h = lbv.config(hidden=64, intermediate=64, num_experts=8, n_group=2, topk_group=1, top_k=2)
+    assert lbv.lbv_moe_permute_workspace_size(small_h, (1 << 24) - 1) > 0
+    with pytest.raises(lbv.LbvError) as e:
+        lbv.lbv_moe_permute_workspace_size(small_h, 1 << 24)
+    assert e.value.status == lbv.LBV_ERR_SHAPE
     wide = dict(hidden=1 << 15, intermediate=1 << 14, n_shared_experts=2)   # shared_w13 4 GiB
     assert lbv.lbv_moe_check_config(lbv.config(**wide)) == lbv.LBV_ERR_SHAPE
     assert lbv.lbv_moe_check_config(lbv.config(**dict(wide, n_shared_experts=1))) == lbv.LBV_OK
