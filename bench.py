@@ -28,9 +28,9 @@ HBM_PEAK_GBS = 8000.0
 # default_gen_T38000: rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch,
 # two --pmc runs of `bench.py --copy-calibration`), each scaled by what the same
 # counter reads for a plain 1 GiB device copy (FETCH_SIZE x 2.000, WRITE_SIZE
-# x 1.000): 3,484,505 KiB x 2 read + 513,000 KiB written.  Re-measure whenever
+# x 1.000): 3,297,198 KiB x 2 read + 556,954 KiB written.  Re-measure whenever
 # the kernel changes (None then).
-GEMM_W13_TRAFFIC_BYTES = 7.6614e9
+GEMM_W13_TRAFFIC_BYTES = 7.3228e9
 
 
 def parse():
