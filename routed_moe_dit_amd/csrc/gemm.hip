@@ -45,7 +45,10 @@
 // COMB_CHUNKS / COMB_NT: 16-byte chunks per lane per combine step, and
 // non-temporal combine loads;
 // G*_WAVES: waves per workgroup (4 or 8); G*_COPY_WAVES: waves that issue
-// the stage copies.
+// the stage copies; G*_ORDER: tile order, 0 = m-tile major (the n-tiles of
+// an m-tile adjacent), 1 = n-tile major inside each segment (measured: 0 is
+// better for the gate/up matmul, whose n-tiles share gathered token rows; 1
+// slightly better for the down matmul).
 #ifndef LBV_NPRE
 #define LBV_NPRE 8
 #endif
@@ -72,6 +75,12 @@
 #endif
 #ifndef LBV_EPI_NT
 #define LBV_EPI_NT 1
+#endif
+#ifndef LBV_G1_ORDER
+#define LBV_G1_ORDER 0
+#endif
+#ifndef LBV_G2_ORDER
+#define LBV_G2_ORDER 1
 #endif
 #ifndef LBV_G1_BM
 #define LBV_G1_BM 256
@@ -175,7 +184,7 @@ constexpr int kMaxSeg = 512;
 // one continuous k-loop over all its tiles: the copies of the next tile's
 // first k-tile are issued during the current tile's last k-tile and land
 // while its epilogue runs.
-template <int BM, int BN, int MODE, int NW, int CWV>
+template <int BM, int BN, int MODE, int NW, int CWV, int ORDER>
 __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     // NW waves: 2 along the tokens x NW/2 along the weight rows (NW = 4: one
     // wave per SIMD with 128 x 128 accumulators; NW = 8: two per SIMD with
@@ -258,11 +267,24 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     // pointer only moves forward ------------------------------------------------
     int walk = 0;
     auto locate = [&](int tt, int& seg_, int& m0_, int& nt_) {
-        const int mt = tt / a.ntn;
-        nt_ = tt - mt * a.ntn;
-        while (__builtin_amdgcn_readfirstlane(s_pre[walk + 1]) <= mt) ++walk;
-        seg_ = walk;
-        m0_ = (mt - __builtin_amdgcn_readfirstlane(s_pre[walk])) * BM;
+        if (ORDER == 0) {
+            // m-tile major: the n-tiles of one m-tile are adjacent
+            const int mt = tt / a.ntn;
+            nt_ = tt - mt * a.ntn;
+            while (__builtin_amdgcn_readfirstlane(s_pre[walk + 1]) <= mt) ++walk;
+            seg_ = walk;
+            m0_ = (mt - __builtin_amdgcn_readfirstlane(s_pre[walk])) * BM;
+        } else {
+            // inside a segment n-tile major: the m-tiles that share one
+            // weight slice are adjacent
+            while (__builtin_amdgcn_readfirstlane(s_pre[walk + 1]) * a.ntn <= tt) ++walk;
+            seg_ = walk;
+            const int p0 = __builtin_amdgcn_readfirstlane(s_pre[walk]);
+            const int nm = __builtin_amdgcn_readfirstlane(s_pre[walk + 1]) - p0;
+            const int loc = tt - p0 * a.ntn;
+            nt_ = loc / nm;
+            m0_ = (loc - nt_ * nm) * BM;
+        }
     };
 
     // ---- copy sources: a wave-uniform base (scalar registers, advanced by BK
@@ -848,7 +870,7 @@ hipError_t launch_gemm_w13(const Dims& d, const void* x, const void* w13,
     a.ncols = d.I;
     if (d.bf16) {
         a.ntn = (d.I + G1_BN / 2 - 1) / (G1_BN / 2);
-        hipLaunchKernelGGL((gemm_bf16_kernel<G1_BM, G1_BN, 0, LBV_G1_WAVES, LBV_G1_COPY_WAVES>), dim3(cu_count() / 8 * 8),
+        hipLaunchKernelGGL((gemm_bf16_kernel<G1_BM, G1_BN, 0, LBV_G1_WAVES, LBV_G1_COPY_WAVES, LBV_G1_ORDER>), dim3(cu_count() / 8 * 8),
                            dim3(LBV_G1_WAVES * 64), 0, stream, a);
     } else {
         a.ntn = (d.I + 31) / 32;
@@ -873,7 +895,7 @@ hipError_t launch_gemm_w2(const Dims& d, const void* act, const void* w2, const 
     a.ncols = d.H;
     if (d.bf16) {
         a.ntn = (d.H + G2_BN - 1) / G2_BN;
-        hipLaunchKernelGGL((gemm_bf16_kernel<G2_BM, G2_BN, 1, LBV_G2_WAVES, LBV_G2_COPY_WAVES>), dim3(cu_count() / 8 * 8),
+        hipLaunchKernelGGL((gemm_bf16_kernel<G2_BM, G2_BN, 1, LBV_G2_WAVES, LBV_G2_COPY_WAVES, LBV_G2_ORDER>), dim3(cu_count() / 8 * 8),
                            dim3(LBV_G2_WAVES * 64), 0, stream, a);
     } else {
         a.ntn = (d.H + 31) / 32;
