@@ -263,20 +263,22 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     int t = static_cast<int>(static_cast<int64_t>(NT) * xcd / 8) + slot;
     if (t >= c1) return;
 
-    // ---- tile lookup: tiles are visited in increasing order, so the segment
-    // pointer only moves forward ------------------------------------------------
+    // ---- tile lookup: a forward walk over the segment table from the last
+    // tile's segment (restarted from 0 if a tile index goes backwards) ----------
     int walk = 0;
     auto locate = [&](int tt, int& seg_, int& m0_, int& nt_) {
         if (ORDER == 0) {
             // m-tile major: the n-tiles of one m-tile are adjacent
             const int mt = tt / a.ntn;
             nt_ = tt - mt * a.ntn;
+            if (__builtin_amdgcn_readfirstlane(s_pre[walk]) > mt) walk = 0;   // went backwards
             while (__builtin_amdgcn_readfirstlane(s_pre[walk + 1]) <= mt) ++walk;
             seg_ = walk;
             m0_ = (mt - __builtin_amdgcn_readfirstlane(s_pre[walk])) * BM;
         } else {
             // inside a segment n-tile major: the m-tiles that share one
             // weight slice are adjacent
+            if (__builtin_amdgcn_readfirstlane(s_pre[walk]) * a.ntn > tt) walk = 0;   // went backwards
             while (__builtin_amdgcn_readfirstlane(s_pre[walk + 1]) * a.ntn <= tt) ++walk;
             seg_ = walk;
             const int p0 = __builtin_amdgcn_readfirstlane(s_pre[walk]);
