@@ -289,17 +289,19 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
 // bf16, so each product x*plane is exact in fp32 and the MFMA sums them in
 // fp32: the logit is an fp32 dot product, in a different summation order.
 //
-// One workgroup routes TOK = 32 TM tokens (TM chosen per call so that the
-// grid fills the CUs in one round where it can).  Per 64-wide hidden slice a
-// stage holds the TOK x rows and the 3 x EP plane rows (128 bytes each, laid
-// out [X0|X1|W0|W1] over two stages), filled by asynchronous copies that are
-// spread one by one between the MFMAs of the previous slice.  Wave w owns
-// expert tile w % (EP/32) (32 experts) against all TM token tiles: 3 planes x
-// TM MFMAs per 16-deep step.  The epilogue turns logits into scores
-// s = sigmoid(z) in LDS; then each lane routes one token by scanning its row
-// with selection values c = s + bias: in-group top-2 sums, kept groups, and a
-// sorted top-K insertion in (c descending, id ascending) order over the kept
-// groups' experts.
+// One workgroup (8 waves, two per SIMD) routes TOK = 32 TM tokens (TM chosen
+// per call so that the grid fills the CUs in one round where it can).  Per
+// 64-wide hidden slice a stage holds the TOK x rows and the 3 x EP plane rows
+// (128 bytes each, laid out [X0|X1|W0|W1] over two stages), filled by
+// asynchronous copies that waves 0-3 spread between their MFMAs.  Wave w owns
+// expert tile (w % 4) % (EP/32) against all TM token tiles and the 16-deep
+// slices 2g, 2g+1 (g = w / 4) of every hidden slice: 3 planes x TM MFMAs per
+// step; the two halves of each logit are added through LDS at the end.  The
+// epilogue turns logits into scores s = sigmoid(z) in LDS; then two lanes
+// route one token with selection values c = s + bias: in-group top-2 sums,
+// kept groups, and a sorted top-K in (c descending, id ascending) order over
+// the kept groups' experts, kept as 64-bit keys so that the insertion has no
+// branches.
 
 constexpr int RV_NGMAX = 8;
 constexpr int RV_BK = 64;
@@ -334,7 +336,7 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* wr, uint
 __device__ __forceinline__ int rswz(int r) { return (r >> 1) & 7; }
 
 template <int TM, int EP, int KMAX>
-__global__ __launch_bounds__(256) void route_bf16_kernel(RouteV2Args a) {
+__global__ __launch_bounds__(512) void route_bf16_kernel(RouteV2Args a) {
     typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
     typedef float f32x16 __attribute__((ext_vector_type(16)));
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -355,6 +357,12 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(RouteV2Args a) {
     const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TOK;
     const int H = a.H, E = a.E;
     if (tid < EP) s_bias[tid] = tid < E ? a.bias[tid] : 0.f;
+    // 8 waves, two per SIMD: wave w handles expert tile (w % 4) % (EP / 32)
+    // and the 16-deep slices 2g, 2g+1 (g = w / 4) of every 64-wide k-tile;
+    // waves 0-3 also issue all the copies.  The two halves of the sum meet in
+    // LDS at the end.
+    const int grp = wave >> 2, ew = wave & 3;
+    const bool copier = wave < 4;
 
     // ---- copy sources: a uniform base plus 32-bit per-lane byte offsets.  X
     // copy i of wave w fills x rows w*TOK/4 + 8i + lane/8; W copy i fills plane
@@ -363,7 +371,7 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(RouteV2Args a) {
     uint32_t xoff[XI], woff[WI];
 #pragma unroll
     for (int i = 0; i < XI; ++i) {
-        const int r = wave * (TOK / 4) + i * 8 + (lane >> 3);
+        const int r = ew * (TOK / 4) + i * 8 + (lane >> 3);
         const uint32_t c = (lane & 7) ^ rswz(r);
         int64_t t = t0 + r;
         if (t >= a.T) t = a.T - 1;
@@ -371,7 +379,7 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(RouteV2Args a) {
     }
 #pragma unroll
     for (int i = 0; i < WI; ++i) {
-        const int q = wave * (3 * EP / 4) + i * 8 + (lane >> 3);
+        const int q = ew * (3 * EP / 4) + i * 8 + (lane >> 3);
         const uint32_t c = (lane & 7) ^ rswz(q);
         const int p = q / EP;
         int e = q % EP;
@@ -382,6 +390,7 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(RouteV2Args a) {
     uint16_t* const ws = smem + 2 * XSZ;                  // W0, W1
     auto copies = [&](auto S, int kt, int d0, int d1) {
         constexpr int s = decltype(S)::value;
+        if (!copier) return;
         static_for<NI>([&](auto D) {
             constexpr int d = decltype(D)::value;
             if (d >= d0 && d < d1) {
@@ -399,23 +408,23 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(RouteV2Args a) {
         const u32x4 z = {0u, 0u, 0u, 0u};
         u32x4* px = reinterpret_cast<u32x4*>(xs + s * XSZ);
         u32x4* pw = reinterpret_cast<u32x4*>(ws + s * WSZ);
-        for (int q = tid; q < XSZ / 8; q += 256) px[q] = z;
-        for (int q = tid; q < WSZ / 8; q += 256) pw[q] = z;
+        for (int q = tid; q < XSZ / 8; q += 512) px[q] = z;
+        for (int q = tid; q < WSZ / 8; q += 512) pw[q] = z;
     };
 
     // ---- fragments: plane rows are the MFMA's first operand, token rows the
     // second; slice kk of stage s: x fragment i at fx[kk] + s*XSZ + 32*i*BK,
     // plane p at fw[kk] + s*WSZ + p*EP*BK --------------------------------------
     const int kh = lane >> 5, rl = lane & 31;
-    const int et = wave % (EP / 32);                      // expert tile (EP = 64: waves 2, 3 repeat 0, 1)
-    const uint16_t* fx[4];
-    const uint16_t* fw[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        const int ch = kk * 2 + kh;
-        fx[kk] = xs + rl * BK + ((ch ^ rswz(rl)) * 8);
-        fw[kk] = ws + (et * 32 + rl) * BK + ((ch ^ rswz(rl)) * 8);
-    }
+    const int et = ew % (EP / 32);                        // expert tile (EP = 64: waves 2, 3 repeat 0, 1)
+    const int ka = 2 * grp, kb = 2 * grp + 1;             // this wave's slices of a k-tile
+    // fragment pointers of slice kk: fx + s*XSZ + 32*i*BK, fw + s*WSZ + p*EP*BK
+    auto fxp = [&](int kk) { return xs + rl * BK + (((kk * 2 + kh) ^ rswz(rl)) * 8); };
+    auto fwp = [&](int kk) { return ws + (et * 32 + rl) * BK + (((kk * 2 + kh) ^ rswz(rl)) * 8); };
+    const uint16_t* const fxa = fxp(ka);
+    const uint16_t* const fwa = fwp(ka);
+    const uint16_t* const fxb = fxp(kb);
+    const uint16_t* const fwb = fwp(kb);
     f32x16 acc[TM];
 #pragma unroll
     for (int i = 0; i < TM; ++i) acc[i] = f32x16{};
@@ -429,43 +438,42 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(RouteV2Args a) {
     wait_vmcnt<0>();
     block_barrier();
 #pragma unroll
-    for (int i = 0; i < TM; ++i) tf0[i] = *reinterpret_cast<const bf16x8*>(fx[0] + i * 32 * BK);
+    for (int i = 0; i < TM; ++i) tf0[i] = *reinterpret_cast<const bf16x8*>(fxa + i * 32 * BK);
 #pragma unroll
-    for (int p = 0; p < 3; ++p) wf0[p] = *reinterpret_cast<const bf16x8*>(fw[0] + p * EP * BK);
+    for (int p = 0; p < 3; ++p) wf0[p] = *reinterpret_cast<const bf16x8*>(fwa + p * EP * BK);
 
     constexpr int NQ = 3 * TM;                            // MFMAs per slice
     constexpr int NR = TM + 3;                            // fragment reads per slice
     constexpr int NPRE = NQ - NR;                         // MFMAs of the last slice before the barrier
     static_assert(NPRE >= 2, "reads fit between the MFMAs");
     // one slice: MFMAs from (CT, CW), after MFMA Q0 + r the fragment read r of
-    // slice NKK of stage NB into (NT, NW), copies [D0, D1) of k-tile KF spread
-    // over the MFMAs
-#define RV_SLICE(CT, CW, NT_, NW_, NB, NKK, Q0, Q1, TS, KF, DO_COPY, D0, D1)                    \
+    // the slice at (FX, FW) of stage NB into (NT, NW), copies [D0, D1) of
+    // k-tile KF spread over the MFMAs
+#define RV_SLICE(CT, CW, NT_, NW_, NB, FX, FW, Q0, Q1, TS, KF, DO_COPY, D0, D1)                 \
     _Pragma("unroll") for (int q = (Q0); q < (Q1); ++q) {                                      \
         acc[q % TM] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(CW[q / TM], CT[q % TM], acc[q % TM], 0, 0, 0); \
         const int r_ = q - (Q0);                                                                \
         if (r_ < TM)                                                                            \
-            NT_[r_] = *reinterpret_cast<const bf16x8*>(fx[NKK] + (NB) * XSZ + r_ * 32 * BK);    \
+            NT_[r_] = *reinterpret_cast<const bf16x8*>((FX) + (NB) * XSZ + r_ * 32 * BK);       \
         else if (r_ < NR)                                                                       \
-            NW_[r_ - TM] = *reinterpret_cast<const bf16x8*>(fw[NKK] + (NB) * WSZ + (r_ - TM) * EP * BK); \
+            NW_[r_ - TM] = *reinterpret_cast<const bf16x8*>((FW) + (NB) * WSZ + (r_ - TM) * EP * BK); \
         if ((DO_COPY) && (D1) > (D0)) {                                                         \
             const int per = ((D1) - (D0) + (Q1) - (Q0) - 1) / ((Q1) - (Q0));                    \
             copies(TS, KF, (D0) + r_ * per, (D0) + r_ * per + per < (D1) ? (D0) + r_ * per + per : (D1)); \
         }                                                                                       \
         __builtin_amdgcn_sched_barrier(0);                                                      \
     }
-    // k-tile kt in stage S: slices 0 and 1 carry the copies of k-tile kt + 1
-    // into the other stage (freed by k-tile kt - 1); the last slice brackets
-    // the hand-over (wait, barrier, then reads of slice 0 of k-tile kt + 1)
+    // k-tile kt in stage S: the wave's first slice carries the copies of
+    // k-tile kt + 1 into the other stage (freed by k-tile kt - 1); its second
+    // slice brackets the hand-over (wait, barrier, then the reads of the
+    // wave's first slice of k-tile kt + 1)
     auto step = [&](auto S, int kt) {
         constexpr int SI = decltype(S)::value;
         const auto TS = std::integral_constant<int, 1 - SI>{};
         const int kf = kt + 1;
         const bool do_copy = kf < nk;
         if (kf >= nk && kf < nkp) zero_fill(TS);
-        RV_SLICE(tf0, wf0, tf1, wf1, SI, 1, 0, NQ, TS, kf, do_copy, 0, NI / 2)
-        RV_SLICE(tf1, wf1, tf0, wf0, SI, 2, 0, NQ, TS, kf, do_copy, NI / 2, NI)
-        RV_SLICE(tf0, wf0, tf1, wf1, SI, 3, 0, NQ, TS, kf, false, 0, 0)
+        RV_SLICE(tf0, wf0, tf1, wf1, SI, fxb, fwb, 0, NQ, TS, kf, do_copy, 0, NI)
 #pragma unroll
         for (int q = 0; q < NPRE; ++q)
             acc[q % TM] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf1[q / TM], tf1[q % TM], acc[q % TM], 0, 0, 0);
@@ -476,7 +484,7 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(RouteV2Args a) {
             block_barrier();
         }
         __builtin_amdgcn_sched_barrier(0);
-        RV_SLICE(tf1, wf1, tf0, wf0, 1 - SI, 0, NPRE, NQ, TS, kf, false, 0, 0)
+        RV_SLICE(tf1, wf1, tf0, wf0, 1 - SI, fxa, fwa, NPRE, NQ, TS, kf, false, 0, 0)
     };
 #undef RV_SLICE
     for (int kt = 0; kt < nkp; kt += 2) {
@@ -484,9 +492,29 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(RouteV2Args a) {
         step(S1{}, kt + 1);
     }
 
-    // ---- scores to LDS: lane holds experts 8q + 4*kh + [0,4) of token rl ----
+    // ---- the two halves of the sum: waves 4-7 hand theirs to waves 0-3 ----
     wait_lgkmcnt0();
     block_barrier();
+    {
+        float* part = reinterpret_cast<float*>(smem);     // [4][TM][16][64]
+        static_assert(4 * TM * 16 * 64 * 4 <= SMEM, "partial sums fit in the stage memory");
+        if (grp == 1) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) part[((ew * TM + i) * 16 + v) * 64 + lane] = acc[i][v];
+        }
+        __syncthreads();
+        if (grp == 0) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][v] += part[((ew * TM + i) * 16 + v) * 64 + lane];
+        }
+        __syncthreads();
+    }
+
+    // ---- scores to LDS: lane holds experts 8q + 4*kh + [0,4) of token rl ----
     float* Ss = reinterpret_cast<float*>(smem);
     if (wave < EP / 32) {
 #pragma unroll
@@ -504,33 +532,36 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(RouteV2Args a) {
     }
     __syncthreads();
 
-    // ---- selection: lane-per-token, c = s + bias ------------------------------
-    const int tok = tid;
-    if (tok >= TOK) return;
+    // ---- selection: two lanes per token (u = 0, 1), lane u taking experts
+    // 4b + 2u and 4b + 2u + 1 of every block of four; c = s + bias ---------------
+    const int tok = tid >> 1, u = tid & 1;
+    if (tok >= TOK) return;                               // both lanes of a token alike
     const int64_t t = t0 + tok;
     if (t >= a.T) return;
     const float* srow = Ss + tok * PITCH;
     const int G = a.G, NG = a.NG;
 
-    // in-group top-2 sums
+    // in-group top-2 sums: each lane's top-2 over its half, then the top-2 of
+    // the four (max / min, no branches); both lanes end with the same sums
     float gsc[RV_NGMAX];
 #pragma unroll
     for (int j = 0; j < RV_NGMAX; ++j) {
         gsc[j] = -INFINITY;
         if (j < NG) {
             float b1 = -INFINITY, b2 = -INFINITY;
-            for (int e = j * G; e < (j + 1) * G; e += 4) {
-                const float4 v4 = *reinterpret_cast<const float4*>(srow + e);
-                const float4 b4 = *reinterpret_cast<const float4*>(s_bias + e);
-                const float vv[4] = {v4.x + b4.x, v4.y + b4.y, v4.z + b4.z, v4.w + b4.w};
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const float v = vv[u];
-                    if (v > b1) { b2 = b1; b1 = v; }
-                    else if (v > b2) { b2 = v; }
-                }
+            for (int e0 = j * G; e0 < (j + 1) * G; e0 += 4) {
+                const int e = e0 + 2 * u;
+                const float2 v2 = *reinterpret_cast<const float2*>(srow + e);
+                const float2 bb = *reinterpret_cast<const float2*>(s_bias + e);
+                const float c0 = v2.x + bb.x;
+                const float c1 = v2.y + bb.y;
+                b2 = fmaxf(b2, fminf(b1, c0));
+                b1 = fmaxf(b1, c0);
+                b2 = fmaxf(b2, fminf(b1, c1));
+                b1 = fmaxf(b1, c1);
             }
-            gsc[j] = b1 + b2;
+            const float p1 = __shfl_xor(b1, 1), p2 = __shfl_xor(b2, 1);
+            gsc[j] = fmaxf(b1, p1) + fmaxf(fminf(b1, p1), fmaxf(b2, p2));
         }
     }
     // kept groups: repeated arg-max, lower index on ties; then their indices ascending
@@ -539,41 +570,63 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(RouteV2Args a) {
         float bv = -INFINITY;
         int bj = -1;
 #pragma unroll
-        for (int j = 0; j < RV_NGMAX; ++j)
-            if (j < NG && !((kept >> j) & 1u) && (bj < 0 || gsc[j] > bv)) { bv = gsc[j]; bj = j; }
+        for (int j = 0; j < RV_NGMAX; ++j) {
+            const bool take = j < NG && !((kept >> j) & 1u) && (bj < 0 || gsc[j] > bv);
+            bv = take ? gsc[j] : bv;
+            bj = take ? j : bj;
+        }
         kept |= 1u << bj;
     }
-    // top-K (first KMAX) over the kept groups' experts in ascending id order
-    float v[KMAX];
-    int id[KMAX];
+    // top-K (first KMAX) in (c descending, id ascending) order, as 64-bit
+    // keys: an order-preserving image of c (with -0 taken as +0) above the
+    // complement of the id, so that the larger key is the larger c, or the
+    // lower id on equal c.  A sorted insertion is then
+    // key[k] = max(key[k], min(key[k-1], new)).  Each lane inserts its half
+    // of the kept groups' experts, then the partner's list.
+    auto okey = [](float c, int e) -> uint64_t {
+        uint32_t b = __float_as_uint(c + 0.0f);
+        b ^= static_cast<uint32_t>(static_cast<int32_t>(b) >> 31) | 0x80000000u;
+        return (static_cast<uint64_t>(b) << 32) | static_cast<uint32_t>(~e);
+    };
+    uint64_t key[KMAX];
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) { v[k] = -INFINITY; id[k] = -1; }
+    for (int k = 0; k < KMAX; ++k) key[k] = 0;           // below every real key; decodes to id -1
+    auto insert = [&](uint64_t nk) {
+#pragma unroll
+        for (int k = KMAX - 1; k > 0; --k) {
+            const uint64_t lo = key[k - 1] < nk ? key[k - 1] : nk;
+            key[k] = key[k] > lo ? key[k] : lo;
+        }
+        key[0] = key[0] > nk ? key[0] : nk;
+    };
     uint32_t rem = kept;
     for (int r = 0; r < a.TG; ++r) {
         const int j = __builtin_ctz(rem);
         rem &= rem - 1;
-        for (int e = j * G; e < (j + 1) * G; e += 4) {
-            const float4 v4 = *reinterpret_cast<const float4*>(srow + e);
-            const float4 b4 = *reinterpret_cast<const float4*>(s_bias + e);
-            const float vv[4] = {v4.x + b4.x, v4.y + b4.y, v4.z + b4.z, v4.w + b4.w};
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float c = vv[u];
-                const int ec = e + u;
-#pragma unroll
-                for (int k = KMAX - 1; k > 0; --k) {
-                    const bool gp = c > v[k - 1];
-                    const bool gk = c > v[k];
-                    const float nv = gp ? v[k - 1] : (gk ? c : v[k]);
-                    const int ni = gp ? id[k - 1] : (gk ? ec : id[k]);
-                    v[k] = nv;
-                    id[k] = ni;
-                }
-                if (c > v[0]) { v[0] = c; id[0] = ec; }
-            }
+        for (int e0 = j * G; e0 < (j + 1) * G; e0 += 4) {
+            const int e = e0 + 2 * u;
+            const float2 v2 = *reinterpret_cast<const float2*>(srow + e);
+            const float2 bb = *reinterpret_cast<const float2*>(s_bias + e);
+            insert(okey(v2.x + bb.x, e));
+            insert(okey(v2.y + bb.y, e + 1));
         }
     }
-    // weights from the raw scores, slot order sum, scaled once
+    {
+        uint64_t pk[KMAX];
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            const uint32_t hi = __shfl_xor(static_cast<uint32_t>(key[k] >> 32), 1);
+            const uint32_t lo = __shfl_xor(static_cast<uint32_t>(key[k]), 1);
+            pk[k] = (static_cast<uint64_t>(hi) << 32) | lo;
+        }
+#pragma unroll
+        for (int m = 0; m < KMAX; ++m) insert(pk[m]);
+    }
+    int id[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) id[k] = static_cast<int>(~static_cast<uint32_t>(key[k]));
+    // weights from the raw scores, slot order sum, scaled once; lane u stores
+    // the slots k with k % 2 == u
     const bool valid = a.mask == nullptr || a.mask[t] != 0;
     float sk[KMAX];
     float sum = 0.f;
@@ -587,7 +640,7 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(RouteV2Args a) {
     }
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
-        if (k < a.K) {
+        if (k < a.K && (k & 1) == u) {
             float wv = a.norm ? sk[k] / sum : sk[k];
             wv = wv * a.rsf;
             a.ids[t * a.K + k] = valid ? id[k] : -1;
@@ -641,7 +694,7 @@ hipError_t launch_route(const Dims& d, const void* x, const float* router_w, con
         }
         const dim3 grid(static_cast<unsigned>((d.T + 32 * tm - 1) / (32 * tm)));
 #define RV_LAUNCH(TM_, EP_, KM_) \
-        hipLaunchKernelGGL((route_bf16_kernel<TM_, EP_, KM_>), grid, dim3(256), 0, stream, a)
+        hipLaunchKernelGGL((route_bf16_kernel<TM_, EP_, KM_>), grid, dim3(512), 0, stream, a)
 #define RV_BY_TM(EP_, KM_)                    \
         if (tm == 4) RV_LAUNCH(4, EP_, KM_);  \
         else if (tm == 5) RV_LAUNCH(5, EP_, KM_); \
