@@ -94,6 +94,40 @@ def test_route_parity_full_size(wl):
     print("route %s: near-tie %d of %d, mismatched %d" % (wl.name, near.sum(), wl.T, (~same).sum()))
 
 
+TIE_CASES = [W[1], var("E64_pairs", num_experts=64, n_group=4, topk_group=2, top_k=6, T=257),
+             var("E256_pairs", num_experts=256, n_group=8, topk_group=4, top_k=8, T=333, hidden=256),
+             var("E16_pairs_f32", num_experts=16, n_group=4, topk_group=2, top_k=4, T=65, hidden=64,
+                 dtype="f32")]
+
+
+@pytest.mark.parametrize("wl", TIE_CASES, ids=lambda w: w.name)
+def test_route_exact_ties_break_to_lower_id(wl):
+    """Experts 2m and 2m+1 get the same router row and bias, so their fp32
+    logits, scores and selection values are bitwise equal (one expert tile
+    computes both from identical operands).  Ties go to the lower id: 2m+1 is
+    chosen only together with 2m, and the pair gets equal weights; the oracle
+    obeys the same rule, and tokens with clear margins match it."""
+    note("route ties %s" % wl.name)
+    inp = synth.make_inputs(wl)
+    rw, b = inp["router_w"].copy(), inp["e_bias"].copy()
+    rw[1::2] = rw[0::2]
+    b[1::2] = b[0::2]
+    d = upload(wl, inp)
+    d["router_w"], d["e_bias"] = dev(rw, "f32"), dev(b, "f32")
+    g_ids, g_w = run_route(wl, d)
+    o = oracle.route(wl, inp["x"], rw, b, inp["mask"])
+    for ids, ws in ((g_ids, g_w), (o["ids"], o["w"])):
+        for row, wrow in zip(ids, ws):
+            chosen = dict(zip(row.tolist(), wrow.tolist()))
+            for e in chosen:
+                if e >= 0 and e % 2 == 1:
+                    assert e - 1 in chosen, (row, wl.name)
+                    assert chosen[e] == chosen[e - 1]
+    same, near = compare_routing(g_ids, g_w, o)
+    print("route ties %s: near-tie %d of %d, mismatched %d" % (wl.name, near.sum(), len(g_ids),
+                                                             (~same).sum()))
+
+
 @pytest.mark.parametrize("T,E,K,ns", [(1, 16, 4, 1), (255, 128, 8, 1), (256, 128, 8, 1),
                                       (257, 128, 8, 0), (1000, 64, 6, 2), (38000, 128, 8, 1)])
 def test_permute_parity(T, E, K, ns):
