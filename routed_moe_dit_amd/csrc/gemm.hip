@@ -45,10 +45,9 @@
 // COMB_CHUNKS / COMB_NT: 16-byte chunks per lane per combine step, and
 // non-temporal combine loads;
 // G*_WAVES: waves per workgroup (4 or 8); G*_COPY_WAVES: waves that issue
-// the stage copies; G*_ORDER: tile order, 0 = m-tile major (the n-tiles of
-// an m-tile adjacent), 1 = n-tile major inside each segment (measured: 0 is
-// better for the gate/up matmul, whose n-tiles share gathered token rows; 1
-// slightly better for the down matmul).
+// the stage copies; G*_ORDER: m-tiles per block of the tile order (1: m-tile
+// major, the n-tiles of an m-tile adjacent; large: n-tile major inside each
+// segment).
 #ifndef LBV_NPRE
 #define LBV_NPRE 8
 #endif
@@ -77,10 +76,10 @@
 #define LBV_EPI_NT 1
 #endif
 #ifndef LBV_G1_ORDER
-#define LBV_G1_ORDER 0
+#define LBV_G1_ORDER 1
 #endif
 #ifndef LBV_G2_ORDER
-#define LBV_G2_ORDER 1
+#define LBV_G2_ORDER 1024
 #endif
 #ifndef LBV_G1_BM
 #define LBV_G1_BM 256
@@ -267,26 +266,21 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     // tile's segment (restarted from 0 if a tile index goes backwards) ----------
     int walk = 0;
     auto locate = [&](int tt, int& seg_, int& m0_, int& nt_) {
-        if (ORDER == 0) {
-            // m-tile major: the n-tiles of one m-tile are adjacent
-            const int mt = tt / a.ntn;
-            nt_ = tt - mt * a.ntn;
-            if (__builtin_amdgcn_readfirstlane(s_pre[walk]) > mt) walk = 0;   // went backwards
-            while (__builtin_amdgcn_readfirstlane(s_pre[walk + 1]) <= mt) ++walk;
-            seg_ = walk;
-            m0_ = (mt - __builtin_amdgcn_readfirstlane(s_pre[walk])) * BM;
-        } else {
-            // inside a segment n-tile major: the m-tiles that share one
-            // weight slice are adjacent
-            if (__builtin_amdgcn_readfirstlane(s_pre[walk]) * a.ntn > tt) walk = 0;   // went backwards
-            while (__builtin_amdgcn_readfirstlane(s_pre[walk + 1]) * a.ntn <= tt) ++walk;
-            seg_ = walk;
-            const int p0 = __builtin_amdgcn_readfirstlane(s_pre[walk]);
-            const int nm = __builtin_amdgcn_readfirstlane(s_pre[walk + 1]) - p0;
-            const int loc = tt - p0 * a.ntn;
-            nt_ = loc / nm;
-            m0_ = (loc - nt_ * nm) * BM;
-        }
+        // Inside a segment the m-tiles form blocks of ORDER (the last one
+        // shorter); a block's tiles run n-tile major, so that the tiles that
+        // share one weight slice are adjacent and those that share token rows
+        // lie a block apart.  ORDER = 1 is m-tile major.
+        if (__builtin_amdgcn_readfirstlane(s_pre[walk]) * a.ntn > tt) walk = 0;   // went backwards
+        while (__builtin_amdgcn_readfirstlane(s_pre[walk + 1]) * a.ntn <= tt) ++walk;
+        seg_ = walk;
+        const int p0 = __builtin_amdgcn_readfirstlane(s_pre[walk]);
+        const int nm = __builtin_amdgcn_readfirstlane(s_pre[walk + 1]) - p0;
+        const int loc = tt - p0 * a.ntn;
+        const int blk = loc / (ORDER * a.ntn);
+        const int r = loc - blk * (ORDER * a.ntn);
+        const int pb = nm - blk * ORDER < ORDER ? nm - blk * ORDER : ORDER;   // m-tiles in this block
+        nt_ = r / pb;
+        m0_ = (blk * ORDER + (r - nt_ * pb)) * BM;
     };
 
     // ---- copy sources: a wave-uniform base (scalar registers, advanced by BK
