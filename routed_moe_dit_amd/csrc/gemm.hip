@@ -48,6 +48,9 @@
 // the stage copies; G*_ORDER: m-tiles per block of the tile order (1: m-tile
 // major, the n-tiles of an m-tile adjacent; large: n-tile major inside each
 // segment).
+#ifndef LBV_MFMA_FENCE
+#define LBV_MFMA_FENCE 1
+#endif
 #ifndef LBV_NPRE
 #define LBV_NPRE 8
 #endif
@@ -475,7 +478,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
                     copy_one(TS, KF, d);                                                       \
             }                                                                                  \
         }                                                                                      \
-        __builtin_amdgcn_sched_barrier(0);                                                     \
+        if (LBV_MFMA_FENCE) __builtin_amdgcn_sched_barrier(0);                                 \
     }
 
     // Next tile (valid when has_next): its lookup is done at the start of the
