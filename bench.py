@@ -153,6 +153,8 @@ def main():
     gemm_flops = flops_w13 + flops_w2
     gemm_ms = stage_ms["gemm_w13_silu"] + stage_ms["gemm_w2_combine"]
     gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    routed_tflops = 6.0 * H * I * R_routed / (gemm_ms * 1e-3) / 1e12
+    valid_tokens = T if inp["mask"] is None else int(inp["mask"].sum())
     w13_tflops = flops_w13 / (stage_ms["gemm_w13_silu"] * 1e-3) / 1e12
     counts = np.bincount(ids_h[ids_h >= 0].reshape(-1), minlength=E)
 
@@ -174,6 +176,8 @@ def main():
                    "intermediate": I, "n_shared": NS, "routed_rows": R_routed},
         "grouped_gemm_tflops": gemm_tflops,
         "grouped_gemm_frac_bf16_peak": gemm_tflops / BF16_PEAK_TFLOPS,
+        "routed_gemm_tflops": routed_tflops,
+        "valid_tokens_per_s": valid_tokens / (ms_per_step * 1e-3),
         "stage_ms": stage_ms,
         "router_x_read_gbs": T * H * (2 if bf else 4) / (stage_ms["route"] * 1e-3) / 1e9,
         "expert_load_max_over_mean": float(counts.max() / max(counts.mean(), 1e-9)),
