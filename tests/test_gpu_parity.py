@@ -403,3 +403,51 @@ def test_zero_tokens_is_noop():
                         torch.empty(0, wl.hidden, dtype=torch.bfloat16, device="cuda"), None, None,
                         ws)
     torch.cuda.synchronize()
+
+
+def test_forward_in_hip_graph_replays_bitwise():
+    """lbv_moe_forward only enqueues kernels on the caller's stream (no
+    allocation, no memset, no host sync), so it can be captured in a HIP
+    graph.  Each replay, with other eager work and synchronisations in between
+    and a changed input, equals the eager call on the same input bitwise."""
+    wl = W[2]
+    note("graph capture %s" % wl.name)
+    inp = synth.make_inputs(wl)
+    d = upload(wl, inp)
+    cfg = cfg_for(wl)
+    T = d["x"].shape[0]
+    x = d["x"].clone()
+    out = torch.empty_like(x)
+    ids = torch.empty(T, wl.top_k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, wl.top_k, dtype=torch.float32, device="cuda")
+    ws = torch.empty(lbv.lbv_moe_workspace_size(cfg, T), dtype=torch.uint8, device="cuda")
+
+    def call():
+        lbv.lbv_moe_forward(cfg, x, d["mask"], d["router_w"], d["e_bias"], d["w13"], d["w2"],
+                            d["shared_w13"], d["shared_w2"], out, ids, w, ws,
+                            torch.cuda.current_stream())
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()                                    # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    for rep in range(4):
+        if rep:
+            # a new input in place, then eager reference work on other buffers
+            x.copy_(d["x"][torch.randperm(T, generator=gen).cuda()])
+        torch.cuda.synchronize()
+        call()
+        torch.cuda.synchronize()
+        ref = (out.clone(), ids.clone(), w.clone())
+        out.zero_()
+        ids.zero_()
+        w.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]) and torch.equal(ids, ref[1]) and torch.equal(w, ref[2]), rep
