@@ -84,6 +84,12 @@
 #ifndef LBV_G2_ORDER
 #define LBV_G2_ORDER 1024
 #endif
+#ifndef LBV_FEW_ROWS
+#define LBV_FEW_ROWS 96
+#endif
+#ifndef LBV_FEW_STAGES
+#define LBV_FEW_STAGES 3
+#endif
 #ifndef LBV_G1_BM
 #define LBV_G1_BM 256
 #endif
@@ -186,7 +192,7 @@ constexpr int kMaxSeg = 512;
 // one continuous k-loop over all its tiles: the copies of the next tile's
 // first k-tile are issued during the current tile's last k-tile and land
 // while its epilogue runs.
-template <int BM, int BN, int MODE, int NW, int CWV, int ORDER>
+template <int BM, int BN, int MODE, int NW, int CWV, int ORDER, int STG>
 __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     // NW waves: 2 along the tokens x NW/2 along the weight rows (NW = 4: one
     // wave per SIMD with 128 x 128 accumulators; NW = 8: two per SIMD with
@@ -206,14 +212,15 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     constexpr int AI = BM / CW / RPI, BI = BN / CW / RPI;  // copies per copying wave per k-tile
     constexpr int NI = AI + BI;
     constexpr int KKS = BK / 16;                 // 16-deep k-slices per k-tile
-    static_assert(BM == 256 && BN == BM, "slot ids: 4 waves x 64 rows; staging split evenly");
+    static_assert(BM % 64 == 0 && BM <= 256 && BN == 256, "slot ids: BM/64 waves x 64 rows");
 
-    // Two stages laid out [A0 | A1 | B0 | B1] (A: token rows, B: weight rows),
-    // so that a fragment read is one base register per slice plus an
-    // immediate offset below 64 KB for the stage and the row group.  Stage 1
-    // (A1 and B1) doubles as the epilogue's staging buffer.
+    // STG stages (2, or 3 for short tiles) laid out [A0 | A1 (| A2) | B0 | B1
+    // (| B2)] (A: token rows, B: weight rows), so that a fragment read is one
+    // base register per slice plus an immediate offset for the stage and the
+    // row group.  Stage STG-1 doubles as the epilogue's staging buffer.
+    static_assert(STG == 2 || STG == 3, "2 or 3 stages");
     constexpr int ASZ = BM * BK, BSZ = BN * BK;  // bf16 elements of one stage's A / B part
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[STG * STAGE];
     __shared__ int s_pre[kMaxSeg + 1];           // m-tiles before segment s
     __shared__ int s_rid[BM];                    // slot ids of a tile's rows: gate/up: the next tile's; down: this tile's
     __shared__ int s_tmp[8];
@@ -299,7 +306,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     // gate/up matmul gathers its x rows by them; the down matmul stores its
     // output rows to them.
     auto rid_copy = [&](int seg_r0_, int seg_n_, int m0_) {
-        if (wave < 4) {
+        if (wave < BM / 64) {
             int m = m0_ + wave * 64 + lane;
             if (m >= seg_n_) m = seg_n_ - 1;
             lds_dma4_sb(a.rows, static_cast<uint32_t>(seg_r0_ + m) * 4, lds_addr(&s_rid[wave * 64]));
@@ -359,13 +366,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     const int a_lds = wave * (BM / CW) * BK;     // this wave's rows inside an A / B part
     const int b_lds = wave * (BN / CW) * BK;
     const int nk = a.kdim / BK;
-    // the k-loop of a tile runs over nkp = nk rounded up to even, so that both
-    // steps of an iteration are unconditional (no MFMA under a branch); the
-    // k-tile past nk is a zero-filled stage, whose products add exact zeros
-    const int nkp = (nk + 1) & ~1;
+    // the k-loop of a tile runs over nkp = nk rounded up to a multiple of STG,
+    // so that every step of an iteration is unconditional (no MFMA under a
+    // branch); the k-tiles past nk are zero-filled stages, whose products add
+    // exact zeros
+    const int nkp = (nk + STG - 1) / STG * STG;
 
     auto a_part = [&](auto S) -> uint16_t* { return lds + decltype(S)::value * ASZ; };
-    auto b_part = [&](auto S) -> uint16_t* { return lds + 2 * ASZ + decltype(S)::value * BSZ; };
+    auto b_part = [&](auto S) -> uint16_t* { return lds + STG * ASZ + decltype(S)::value * BSZ; };
     auto zero_fill = [&](auto S) {
         u32x4* pa = reinterpret_cast<u32x4*>(a_part(S));
         u32x4* pb = reinterpret_cast<u32x4*>(b_part(S));
@@ -409,7 +417,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         for (int kk = 0; kk < KKS; ++kk) {
             const int ch = kk * 2 + kh;                          // swz(r) depends on r mod 32 only
             fa[kk] = lds + ra * BK + ((ch ^ swz<BK>(rl)) * 8);
-            fb[kk] = lds + 2 * ASZ + rb * BK + ((ch ^ swz<BK>(rl)) * 8);
+            fb[kk] = lds + STG * ASZ + rb * BK + ((ch ^ swz<BK>(rl)) * 8);
         }
     };
     // B row of fragment j relative to j = 0
@@ -426,6 +434,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
 
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
 
     // ---- first tile: sources, k-tile 0 into stage 0, first slice read ----------
     int seg, m0, nt;
@@ -438,9 +447,19 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         block_barrier();
     }
     set_sources(seg, seg_r0, seg_n, m0, nt);
+    // k-tiles 0 .. STG-2 into stages 0 .. STG-2 (zero-filled past nk)
+    auto pro_fill = [&](auto S, int kt) {
+        if (kt < nk) {
 #pragma unroll
-    for (int d = 0; d < NI; ++d) copy_one(S0{}, 0, d);
+            for (int d = 0; d < NI; ++d) copy_one(S, kt, d);
+        } else {
+            zero_fill(S);
+        }
+    };
+    pro_fill(S0{}, 0);
+    if constexpr (STG == 3) pro_fill(S1{}, 1);
     wait_vmcnt<0>();
+    wait_lgkmcnt0();
     block_barrier();
 #pragma unroll
     for (int i = 0; i < TM; ++i) tf0[i] = *reinterpret_cast<const bf16x8*>(fa[0] + i * 32 * BK);
@@ -449,8 +468,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
 
     constexpr int NQ = TM * TN;                  // MFMAs per slice
     constexpr int NR = TM + TN;                  // fragment reads per slice
-    constexpr int NPRE = LBV_NPRE < NQ - NR ? LBV_NPRE : NQ - NR;   // MFMAs of the last slice before the barrier
-    static_assert(NQ >= NR + NPRE, "reads fit between the MFMAs");
+    // MFMAs of the last slice before the barrier (0 when a slice has fewer
+    // MFMAs than fragment reads)
+    constexpr int NPRE = NQ - NR <= 0 ? 0 : (LBV_NPRE < NQ - NR ? LBV_NPRE : NQ - NR);
     constexpr int DSL = LBV_COPY_SLICES < KKS - 1 ? LBV_COPY_SLICES : KKS - 1;   // slices carrying copies
 
     // One slice: MFMAs [Q0, Q1) from set (CT, CW) (ZC: the tile's first slice,
@@ -468,10 +488,15 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
             acc[q / TM][q % TM] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                    \
                 CW[q / TM], CT[q % TM], acc[q / TM][q % TM], 0, 0, 0);                        \
         const int r_ = q - (Q0);                                                               \
-        if (r_ < TM)                                                                           \
-            NT_[r_] = *reinterpret_cast<const bf16x8*>(fa[NKK] + (NB) * ASZ + r_ * 32 * BK);  \
-        else if (r_ < NR)                                                                      \
-            NW_[r_ - TM] = *reinterpret_cast<const bf16x8*>(fb[NKK] + (NB) * BSZ + brow(r_ - TM) * BK); \
+        /* read rr goes after MFMA rr, the ones left over after the last MFMA */               \
+        _Pragma("unroll") for (int rr = 0; rr < NR; ++rr) {                                   \
+            if ((rr < (Q1) - (Q0) ? rr : (Q1) - (Q0) - 1) == r_) {                             \
+                if (rr < TM)                                                                   \
+                    NT_[rr] = *reinterpret_cast<const bf16x8*>(fa[NKK] + (NB) * ASZ + rr * 32 * BK); \
+                else                                                                           \
+                    NW_[rr - TM] = *reinterpret_cast<const bf16x8*>(fb[NKK] + (NB) * BSZ + brow(rr - TM) * BK); \
+            }                                                                                  \
+        }                                                                                      \
         if ((D1) > (D0)) {                                                                     \
             _Pragma("unroll") for (int d = (D0); d < (D1); ++d) {                              \
                 if ((d - (D0)) * ((Q1) - (Q0)) / ((D1) > (D0) ? (D1) - (D0) : 1) == r_ && (DO_COPY)) \
@@ -487,23 +512,25 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     bool has_next = false;
     int nseg = 0, nm0 = 0, nnt = 0, nseg_r0 = 0, nseg_n = 0;
 
-    // One k-tile held in stage S.  On entry slice 0 of it is in set 0.
-    // Slices 0 .. DSL-1 also carry the copies of k-tile kt + 1 (or, at the last
-    // k-tile, of the next tile's k-tile 0) into the other stage, which the
-    // previous k-tile freed.  The last slice brackets the hand-over: NPRE
-    // MFMAs, wait for k-tile kt + 1's copies, barrier (every wave is done
-    // reading stage S), then the remaining MFMAs with the reads of slice 0 of
-    // k-tile kt + 1 (unused after the tile's last k-tile).
+    // One k-tile kt held in stage S = kt % STG.  On entry slice 0 of it is in
+    // set 0, and k-tiles kt+1 .. kt+STG-2 are in flight.  Slices 0 .. DSL-1
+    // also carry the copies of k-tile kt + STG - 1 (past the tile's last
+    // k-tile: of the next tile's first ones) into the stage that k-tile
+    // kt - 1 freed.  The last slice brackets the hand-over: NPRE MFMAs, wait
+    // for k-tile kt + 1's copies, barrier (every wave is done reading stage
+    // S), then the remaining MFMAs with the reads of slice 0 of k-tile kt + 1
+    // (unused after the tile's last k-tile).
     auto step = [&](auto S, int kt, auto First) {
         constexpr int SI = decltype(S)::value;
         constexpr bool FIRST = decltype(First)::value;
-        const auto TS = std::integral_constant<int, 1 - SI>{};
-        constexpr int cur = SI, nxt = 1 - SI;   // stages read by this k-tile / the next
-        const int kf = kt + 1;
-        const bool last = kf == nkp;
-        const bool do_copy = kf < nk || (last && has_next);
-        const int kc = last ? 0 : kf;            // k-tile index of the copies
-        if (kf >= nk && !last) zero_fill(TS);
+        const auto TS = std::integral_constant<int, (SI + STG - 1) % STG>{};
+        constexpr int cur = SI, nxt = (SI + 1) % STG;   // stages read by this k-tile / the next
+        const int kf = kt + STG - 1;             // k-tile copied during this step
+        const bool nextc = kf >= nkp;            // ... a k-tile of the next tile
+        const int kc = nextc ? kf - nkp : kf;    // its index within its tile
+        const bool want = !nextc || has_next;    // that k-tile exists
+        const bool do_copy = want && kc < nk;    // past nk it is a zero-filled stage
+        if (want && kc >= nk) zero_fill(TS);
         if (MODE == 0 && kt == 0 && has_next) rid_copy(nseg_r0, nseg_n, nm0);
         if (MODE == 1 && kt == 0) rid_copy(seg_r0, seg_n, m0);
 #pragma unroll
@@ -524,10 +551,15 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
             acc[q / TM][q % TM] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 wf1[q / TM], tf1[q % TM], acc[q / TM][q % TM], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        if (!last) wait_vmcnt<0>();              // k-tile kt + 1 (and any slot-id copy) landed
+        if (kt + 1 < nkp) {
+            // k-tile kt + 1 (and any slot-id copy) landed; with three stages
+            // the copies issued in this step may stay in flight
+            if (STG == 3 && do_copy) wait_vmcnt<NI>();
+            else wait_vmcnt<0>();
+        }
         wait_lgkmcnt0();
         block_barrier();
-        if (kf == nkp - 1 && has_next) {
+        if (kt == nkp - STG && has_next) {
             set_sources(nseg, nseg_r0, nseg_n, nm0, nnt);
             wait_lgkmcnt0();
         }
@@ -538,11 +570,17 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
 
     constexpr int WCOLS = MODE == 0 ? BN / 2 / WN : BN / WN;   // output columns per wave
     constexpr int CHUNKS = WCOLS / 8;                    // 16-byte chunks per row
-    constexpr int RSZ = 2 * ASZ / NW;                    // staging elements per wave (stage 1 split evenly)
-    constexpr int PROWS = RSZ / WCOLS;                   // rows per staging pass
-    constexpr int PT = PROWS / 32;                       // token tiles per pass
+    // staging regions in stage STG-1 (the last one a tile reads): its A and B
+    // parts split evenly when they are the same size, else all in its B part
+    constexpr bool SPLIT = ASZ == BSZ;
+    constexpr int RSZ = SPLIT ? 2 * ASZ / NW : BSZ / NW;   // staging elements per wave
+    constexpr int PT0 = RSZ / WCOLS / 32;
+    constexpr int PT = PT0 < TM ? PT0 : TM;              // token tiles per staging pass
+    constexpr int PROWS = PT * 32;                       // rows per staging pass
     static_assert(PT >= 1 && TM % PT == 0, "whole token tiles per pass");
-    uint16_t* const ep0 = (wave < NW / 2 ? lds + ASZ : lds + 2 * ASZ + BSZ) + (wave % (NW / 2)) * RSZ;   // this wave's staging region
+    constexpr int SL = STG - 1;
+    uint16_t* const ep0 = SPLIT ? (wave < NW / 2 ? lds + SL * ASZ : lds + STG * ASZ + SL * BSZ) + (wave % (NW / 2)) * RSZ
+                                : lds + STG * ASZ + SL * BSZ + wave * RSZ;   // this wave's staging region
     auto ep_off = [&](int row, int col) {                // element offset of (row, col) in the region
         return row * WCOLS + (((col >> 3) ^ (row % CHUNKS)) << 3) + (col & 7);
     };
@@ -561,9 +599,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int i = 0; i < TM; ++i) acc[j][i] = f32x16{};
-        for (int kt = 0; kt < nkp; kt += 2) {
+        for (int kt = 0; kt < nkp; kt += STG) {
             step(S0{}, kt, std::false_type{});
             step(S1{}, kt + 1, std::false_type{});
+            if constexpr (STG == 3) step(S2{}, kt + 2, std::false_type{});
         }
 
         // ---- epilogue: lane holds, for token tile i and weight tile j, output
@@ -572,7 +611,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         // pitch = its column count, 16-byte chunks XOR-swizzled by row), then
         // reads them back 16 bytes per lane, so that every global store
         // instruction writes whole contiguous rows.  Every wave passed the last
-        // barrier after its final reads of stage 1.
+        // barrier after its final reads of stage STG-1.
         const int col0 = MODE == 0 ? nt * (BN / 2) + wn * (BN / 2 / WN) : nt * BN + wn * (BN / WN);
         // staging addresses are formed here, not hoisted out of the tile loop
         // (where they would hold registers through the whole k-loop)
@@ -609,7 +648,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
                     __builtin_amdgcn_sched_barrier(0);   // bounds the accumulators read out at once
                 }
             }
-            if (p == 0) wait_vmcnt<0>();             // the next tile's k-tile 0 landed
+            if (p == 0) wait_vmcnt<0>();             // the next tile's first k-tiles landed
             // read back: lane -> (row, chunk); an instruction covers 64 / CHUNKS rows
             constexpr int RPP = 64 / CHUNKS;
 #pragma unroll
@@ -629,8 +668,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
             }
         }
         if (!has_next) break;
-        // every wave done with its staging reads (stage 1 may be refilled) and
-        // every wave's copies of the next tile's k-tile 0 landed
+        // every wave done with its staging reads (stage STG-1 may be refilled)
+        // and every wave's copies of the next tile's first k-tiles landed
         wait_lgkmcnt0();
         block_barrier();
         // the next tile's copy sources again (they were set for its k-tile 0
@@ -849,6 +888,14 @@ GemmArgs make_args(const Dims& d) {
     return a;
 }
 
+// Few rows per segment on average (T (K + ns) / S < LBV_FEW_ROWS): the
+// matmuls use 64-row tiles, whose copies and MFMAs are a quarter of a
+// 256-row tile's for the A side, instead of padding each expert's few rows
+// to 256.
+bool few_rows(const Dims& d) {
+    return d.T * d.KS < static_cast<int64_t>(LBV_FEW_ROWS) * d.S;
+}
+
 int64_t max_mtiles(const Dims& d, int BM) {
     return (d.T * d.KS + BM - 1) / BM + d.S;
 }
@@ -869,8 +916,12 @@ hipError_t launch_gemm_w13(const Dims& d, const void* x, const void* w13,
     a.ncols = d.I;
     if (d.bf16) {
         a.ntn = (d.I + G1_BN / 2 - 1) / (G1_BN / 2);
-        hipLaunchKernelGGL((gemm_bf16_kernel<G1_BM, G1_BN, 0, LBV_G1_WAVES, LBV_G1_COPY_WAVES, LBV_G1_ORDER>), dim3(cu_count() / 8 * 8),
-                           dim3(LBV_G1_WAVES * 64), 0, stream, a);
+        if (few_rows(d))
+            hipLaunchKernelGGL((gemm_bf16_kernel<64, G1_BN, 0, LBV_G1_WAVES, LBV_G1_COPY_WAVES, LBV_G1_ORDER, LBV_FEW_STAGES>),
+                               dim3(cu_count() / 8 * 8), dim3(LBV_G1_WAVES * 64), 0, stream, a);
+        else
+            hipLaunchKernelGGL((gemm_bf16_kernel<G1_BM, G1_BN, 0, LBV_G1_WAVES, LBV_G1_COPY_WAVES, LBV_G1_ORDER, 2>),
+                               dim3(cu_count() / 8 * 8), dim3(LBV_G1_WAVES * 64), 0, stream, a);
     } else {
         a.ntn = (d.I + 31) / 32;
         const int64_t grid = max_mtiles(d, 32) * a.ntn;
@@ -894,8 +945,12 @@ hipError_t launch_gemm_w2(const Dims& d, const void* act, const void* w2, const 
     a.ncols = d.H;
     if (d.bf16) {
         a.ntn = (d.H + G2_BN - 1) / G2_BN;
-        hipLaunchKernelGGL((gemm_bf16_kernel<G2_BM, G2_BN, 1, LBV_G2_WAVES, LBV_G2_COPY_WAVES, LBV_G2_ORDER>), dim3(cu_count() / 8 * 8),
-                           dim3(LBV_G2_WAVES * 64), 0, stream, a);
+        if (few_rows(d))
+            hipLaunchKernelGGL((gemm_bf16_kernel<64, G2_BN, 1, LBV_G2_WAVES, LBV_G2_COPY_WAVES, LBV_G2_ORDER, LBV_FEW_STAGES>),
+                               dim3(cu_count() / 8 * 8), dim3(LBV_G2_WAVES * 64), 0, stream, a);
+        else
+            hipLaunchKernelGGL((gemm_bf16_kernel<G2_BM, G2_BN, 1, LBV_G2_WAVES, LBV_G2_COPY_WAVES, LBV_G2_ORDER, 2>),
+                               dim3(cu_count() / 8 * 8), dim3(LBV_G2_WAVES * 64), 0, stream, a);
     } else {
         a.ntn = (d.H + 31) / 32;
         const int64_t grid = max_mtiles(d, 32) * a.ntn;
