@@ -106,7 +106,10 @@ lbv_status lbv_moe_check_config(const lbv_moe_config *cfg);
  * Workspace sizes in bytes.
  *   lbv_moe_workspace_size:          for lbv_moe_forward;
  *   lbv_moe_route_workspace_size:    for lbv_moe_route (does not depend on T;
- *                                    3 E H bf16 values on the bf16 path, else 0);
+ *                                    on the bf16 path 3 E H bf16 values, rounded
+ *                                    up to 256 bytes, plus 4 x 4096 x EP fp32
+ *                                    partial logits for calls of at most 4096
+ *                                    tokens, EP = 64 if E <= 64 else 128; else 0);
  *   lbv_moe_permute_workspace_size:  for lbv_moe_permute;
  *   lbv_moe_w2_workspace_size:       for lbv_moe_gemm_w2_combine.
  * Sizes grow linearly with T (the forward one is dominated by the bf16 expert
@@ -133,7 +136,8 @@ lbv_status lbv_moe_w2_workspace_size(const lbv_moe_config *cfg, int64_t T, size_
  *                     weight is split there into three bf16 planes whose sum
  *                     is exactly W_r, so the fp32 logits run on the bf16
  *                     matrix cores; finite W_r entries must stay below the
- *                     bf16 overflow threshold (about 3.39e38).
+ *                     bf16 overflow threshold (about 3.39e38).  Calls of at
+ *                     most 4096 tokens also keep partial logits there.
  * Ties between equal scores go to the lower group / expert index.
  */
 lbv_status lbv_moe_route(const lbv_moe_config *cfg, int64_t T, const void *x,

@@ -65,6 +65,93 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     return v;
 }
 
+// Routes token t with one wave: lane l holds experts e0 = l*EPL + q (q < EPL,
+// EPL <= 4) with raw scores s[q] and selection values c[q] (-inf past E);
+// LG lanes cover one group of G experts.  Group top-2 sums by shuffles, kept
+// groups and the top-K by repeated wave arg-max over (value desc, index asc),
+// weights from the raw scores summed in slot order and scaled once.
+__device__ __forceinline__ void wave_route(int64_t t, int lane, int E, int EPL, int LG, int G,
+                                           int NG, int TG, int K, int norm, float rsf, bool valid,
+                                           const float (&s)[4], const float (&c)[4],
+                                           int32_t* ids, float* w) {
+    const int e0 = lane * EPL;                 // first expert of this lane
+    const int grp = e0 / G;                    // this lane's group (>= NG: no experts)
+    const bool lane_has = e0 < E;
+    // In-group top-2 over this lane's experts, then over the group's LG lanes.
+    float b1 = -INFINITY, b2 = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (q < EPL) {
+            const float v = c[q];
+            if (v > b1) { b2 = b1; b1 = v; }
+            else if (v > b2) { b2 = v; }
+        }
+    }
+    for (int off = 1; off < LG; off <<= 1) {
+        const float o1 = __shfl_xor(b1, off);
+        const float o2 = __shfl_xor(b2, off);
+        const float n1 = fmaxf(b1, o1);
+        const float n2 = fmaxf(fminf(b1, o1), fmaxf(b2, o2));
+        b1 = n1;
+        b2 = n2;
+    }
+    const float gscore = b1 + b2;
+
+    // Keep TG groups: repeated arg-max over (score desc, group asc).
+    uint32_t kept = 0;
+    const bool grp_real = lane_has && grp < NG;
+    for (int rr = 0; rr < TG; ++rr) {
+        uint64_t key = 0;
+        if (grp_real && !((kept >> grp) & 1u))
+            key = (static_cast<uint64_t>(fkey(gscore)) << 32) | (0xffffffffu - static_cast<uint32_t>(grp));
+        key = wave_max_u64(key);
+        const int win = static_cast<int>(0xffffffffu - static_cast<uint32_t>(key));
+        kept |= 1u << win;
+    }
+    const bool in_kept = grp_real && ((kept >> grp) & 1u);
+
+    // Top-K experts in the kept groups: repeated arg-max over (c desc, id asc).
+    uint32_t taken = 0;           // bit q: expert e0+q already chosen
+    int my_id = -1;
+    float my_s = 0.f;
+    for (int k = 0; k < K; ++k) {
+        uint64_t key = 0;
+        if (in_kept) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (q < EPL && !((taken >> q) & 1u) && e0 + q < E) {
+                    const uint64_t kq = (static_cast<uint64_t>(fkey(c[q])) << 32) |
+                                        (0xffffffffu - static_cast<uint32_t>(e0 + q));
+                    key = kq > key ? kq : key;
+                }
+            }
+        }
+        key = wave_max_u64(key);
+        const int win = static_cast<int>(0xffffffffu - static_cast<uint32_t>(key));
+        float sw = 0.f;
+        if (win >= e0 && win < e0 + EPL) {
+            const int q = win - e0;
+            taken |= 1u << q;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq)
+                if (qq == q) sw = s[qq];
+        }
+        // the owner lane's score, broadcast
+        sw = __shfl(sw, win / EPL);
+        if (lane == k) { my_id = win; my_s = sw; }
+    }
+
+    // Weights: sum of the chosen raw scores in slot order, then scale once.
+    float sum = 0.f;
+    for (int k = 0; k < K; ++k) sum += __shfl(my_s, k);
+    if (lane < K) {
+        float wv = norm ? my_s / sum : my_s;
+        wv = wv * rsf;
+        ids[t * K + lane] = valid ? my_id : -1;
+        w[t * K + lane] = valid ? wv : 0.f;
+    }
+}
+
 template <bool XBF16>
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     // LDS: staging of x / W_r chunks, later reused for the logits.
@@ -178,7 +265,6 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     // ---- selection: one wave per token --------------------------------------
     const int EPL = a.EPL, LG = a.LG, G = a.G, K = a.K;
     const int e0 = lane * EPL;                 // first expert of this lane
-    const int grp = e0 / G;                    // this lane's group (>= NG: no experts)
     const bool lane_has = e0 < E;
     float bias_l[4];
 #pragma unroll
@@ -202,79 +288,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
             }
         }
 
-        // In-group top-2 over this lane's experts, then over the group's LG lanes.
-        float b1 = -INFINITY, b2 = -INFINITY;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if (q < EPL) {
-                const float v = c[q];
-                if (v > b1) { b2 = b1; b1 = v; }
-                else if (v > b2) { b2 = v; }
-            }
-        }
-        for (int off = 1; off < LG; off <<= 1) {
-            const float o1 = __shfl_xor(b1, off);
-            const float o2 = __shfl_xor(b2, off);
-            const float n1 = fmaxf(b1, o1);
-            const float n2 = fmaxf(fminf(b1, o1), fmaxf(b2, o2));
-            b1 = n1;
-            b2 = n2;
-        }
-        const float gscore = b1 + b2;
-
-        // Keep TG groups: repeated arg-max over (score desc, group asc).
-        uint32_t kept = 0;
-        const bool grp_real = lane_has && grp < a.NG;
-        for (int rr = 0; rr < a.TG; ++rr) {
-            uint64_t key = 0;
-            if (grp_real && !((kept >> grp) & 1u))
-                key = (static_cast<uint64_t>(fkey(gscore)) << 32) | (0xffffffffu - static_cast<uint32_t>(grp));
-            key = wave_max_u64(key);
-            const int win = static_cast<int>(0xffffffffu - static_cast<uint32_t>(key));
-            kept |= 1u << win;
-        }
-        const bool in_kept = grp_real && ((kept >> grp) & 1u);
-
-        // Top-K experts in the kept groups: repeated arg-max over (c desc, id asc).
-        uint32_t taken = 0;           // bit q: expert e0+q already chosen
-        int my_id = -1;
-        float my_s = 0.f;
-        for (int k = 0; k < K; ++k) {
-            uint64_t key = 0;
-            if (in_kept) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    if (q < EPL && !((taken >> q) & 1u) && e0 + q < E) {
-                        const uint64_t kq = (static_cast<uint64_t>(fkey(c[q])) << 32) |
-                                            (0xffffffffu - static_cast<uint32_t>(e0 + q));
-                        key = kq > key ? kq : key;
-                    }
-                }
-            }
-            key = wave_max_u64(key);
-            const int win = static_cast<int>(0xffffffffu - static_cast<uint32_t>(key));
-            float sw = 0.f;
-            if (win >= e0 && win < e0 + EPL) {
-                const int q = win - e0;
-                taken |= 1u << q;
-#pragma unroll
-                for (int qq = 0; qq < 4; ++qq)
-                    if (qq == q) sw = s[qq];
-            }
-            // the owner lane's score, broadcast
-            sw = __shfl(sw, win / EPL);
-            if (lane == k) { my_id = win; my_s = sw; }
-        }
-
-        // Weights: sum of the chosen raw scores in slot order, then scale once.
-        float sum = 0.f;
-        for (int k = 0; k < K; ++k) sum += __shfl(my_s, k);
-        if (lane < K) {
-            float wv = a.norm ? my_s / sum : my_s;
-            wv = wv * a.rsf;
-            a.ids[t * K + lane] = valid ? my_id : -1;
-            a.w[t * K + lane] = valid ? wv : 0.f;
-        }
+        wave_route(t, lane, E, EPL, LG, G, a.NG, a.TG, K, a.norm, a.rsf, valid, s, c, a.ids, a.w);
     }
 }
 
@@ -334,6 +348,122 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* wr, uint
 
 // 128-byte rows: chunk c of row r at c ^ ((r >> 1) & 7) (conflict-free reads)
 __device__ __forceinline__ int rswz(int r) { return (r >> 1) & 7; }
+
+// Routing of token t by a lane pair (u = 0, 1): srow holds its scores s
+// (LDS), s_bias the correction bias (LDS).  Lane u takes experts 4b + 2u and
+// 4b + 2u + 1 of every block of four; c = s + bias.  Writes ids and weights.
+template <int KMAX>
+__device__ __forceinline__ void select_token(const RouteV2Args& a, const float* srow,
+                                             const float* s_bias, int u, int64_t t) {
+    const int G = a.G, NG = a.NG;
+
+    // in-group top-2 sums: each lane's top-2 over its half, then the top-2 of
+    // the four (max / min, no branches); both lanes end with the same sums
+    float gsc[RV_NGMAX];
+#pragma unroll
+    for (int j = 0; j < RV_NGMAX; ++j) {
+        gsc[j] = -INFINITY;
+        if (j < NG) {
+            float b1 = -INFINITY, b2 = -INFINITY;
+            for (int e0 = j * G; e0 < (j + 1) * G; e0 += 4) {
+                const int e = e0 + 2 * u;
+                const float2 v2 = *reinterpret_cast<const float2*>(srow + e);
+                const float2 bb = *reinterpret_cast<const float2*>(s_bias + e);
+                const float c0 = v2.x + bb.x;
+                const float c1 = v2.y + bb.y;
+                b2 = fmaxf(b2, fminf(b1, c0));
+                b1 = fmaxf(b1, c0);
+                b2 = fmaxf(b2, fminf(b1, c1));
+                b1 = fmaxf(b1, c1);
+            }
+            const float p1 = __shfl_xor(b1, 1), p2 = __shfl_xor(b2, 1);
+            gsc[j] = fmaxf(b1, p1) + fmaxf(fminf(b1, p1), fmaxf(b2, p2));
+        }
+    }
+    // kept groups: repeated arg-max, lower index on ties; then their indices ascending
+    uint32_t kept = 0;
+    for (int r = 0; r < a.TG; ++r) {
+        float bv = -INFINITY;
+        int bj = -1;
+#pragma unroll
+        for (int j = 0; j < RV_NGMAX; ++j) {
+            const bool take = j < NG && !((kept >> j) & 1u) && (bj < 0 || gsc[j] > bv);
+            bv = take ? gsc[j] : bv;
+            bj = take ? j : bj;
+        }
+        kept |= 1u << bj;
+    }
+    // top-K (first KMAX) in (c descending, id ascending) order, as 64-bit
+    // keys: an order-preserving image of c (with -0 taken as +0) above the
+    // complement of the id, so that the larger key is the larger c, or the
+    // lower id on equal c.  A sorted insertion is then
+    // key[k] = max(key[k], min(key[k-1], new)).  Each lane inserts its half
+    // of the kept groups' experts, then the partner's list.
+    auto okey = [](float c, int e) -> uint64_t {
+        uint32_t b = __float_as_uint(c + 0.0f);
+        b ^= static_cast<uint32_t>(static_cast<int32_t>(b) >> 31) | 0x80000000u;
+        return (static_cast<uint64_t>(b) << 32) | static_cast<uint32_t>(~e);
+    };
+    uint64_t key[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) key[k] = 0;           // below every real key; decodes to id -1
+    auto insert = [&](uint64_t nk) {
+#pragma unroll
+        for (int k = KMAX - 1; k > 0; --k) {
+            const uint64_t lo = key[k - 1] < nk ? key[k - 1] : nk;
+            key[k] = key[k] > lo ? key[k] : lo;
+        }
+        key[0] = key[0] > nk ? key[0] : nk;
+    };
+    uint32_t rem = kept;
+    for (int r = 0; r < a.TG; ++r) {
+        const int j = __builtin_ctz(rem);
+        rem &= rem - 1;
+        for (int e0 = j * G; e0 < (j + 1) * G; e0 += 4) {
+            const int e = e0 + 2 * u;
+            const float2 v2 = *reinterpret_cast<const float2*>(srow + e);
+            const float2 bb = *reinterpret_cast<const float2*>(s_bias + e);
+            insert(okey(v2.x + bb.x, e));
+            insert(okey(v2.y + bb.y, e + 1));
+        }
+    }
+    {
+        uint64_t pk[KMAX];
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            const uint32_t hi = __shfl_xor(static_cast<uint32_t>(key[k] >> 32), 1);
+            const uint32_t lo = __shfl_xor(static_cast<uint32_t>(key[k]), 1);
+            pk[k] = (static_cast<uint64_t>(hi) << 32) | lo;
+        }
+#pragma unroll
+        for (int m = 0; m < KMAX; ++m) insert(pk[m]);
+    }
+    int id[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) id[k] = static_cast<int>(~static_cast<uint32_t>(key[k]));
+    // weights from the raw scores, slot order sum, scaled once; lane u stores
+    // the slots k with k % 2 == u
+    const bool valid = a.mask == nullptr || a.mask[t] != 0;
+    float sk[KMAX];
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        sk[k] = 0.f;
+        if (k < a.K) {
+            sk[k] = srow[id[k]];
+            sum += sk[k];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        if (k < a.K && (k & 1) == u) {
+            float wv = a.norm ? sk[k] / sum : sk[k];
+            wv = wv * a.rsf;
+            a.ids[t * a.K + k] = valid ? id[k] : -1;
+            a.w[t * a.K + k] = valid ? wv : 0.f;
+        }
+    }
+}
 
 template <int TM, int EP, int KMAX>
 __global__ __launch_bounds__(512) void route_bf16_kernel(RouteV2Args a) {
@@ -538,115 +668,120 @@ __global__ __launch_bounds__(512) void route_bf16_kernel(RouteV2Args a) {
     if (tok >= TOK) return;                               // both lanes of a token alike
     const int64_t t = t0 + tok;
     if (t >= a.T) return;
-    const float* srow = Ss + tok * PITCH;
-    const int G = a.G, NG = a.NG;
+    select_token<KMAX>(a, Ss + tok * PITCH, s_bias, u, t);
+}
 
-    // in-group top-2 sums: each lane's top-2 over its half, then the top-2 of
-    // the four (max / min, no branches); both lanes end with the same sums
-    float gsc[RV_NGMAX];
+
+// ---------------------------------------------------------------------------
+// Few tokens (T <= RS_TMAX): the logits are split over workgroups along the
+// hidden dimension as well (RS_SPLIT parts), so that short batches fill the
+// chip instead of a few workgroups each walking all of H.  Partial logits go
+// to the workspace; a second kernel adds them in a fixed order, then scores
+// and routes each token with one wave.
+// ---------------------------------------------------------------------------
+constexpr int RS_SPLIT = 4;
+constexpr int RS_TMAX = 4096;
+
+// grid: (ceil(T / 128), EP / 32, RS_SPLIT); 4 waves, wave w owns token tile w
+// against expert tile blockIdx.y (3 planes), hidden k-tiles of part blockIdx.z.
+template <int EP>
+__global__ __launch_bounds__(256) void route_logits_kernel(RouteV2Args a, float* zpart) {
+    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+    typedef float f32x16 __attribute__((ext_vector_type(16)));
+    constexpr int BK = RV_BK;
+    constexpr int TOK = 128, WR = 96, ROWS = TOK + WR;  // x rows, plane rows (3 x 32 experts)
+    constexpr int STAGE = ROWS * BK;
+    constexpr int CI = ROWS / 4 / 8;                    // copies per wave per k-tile (8 rows each)
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TOK;
+    const int et = blockIdx.y, part = blockIdx.z;
+    const int H = a.H, E = a.E;
+    const int nk = H / BK;
+    const int kt0 = nk * part / RS_SPLIT, kt1 = nk * (part + 1) / RS_SPLIT;
+
+    // copy i of wave w: stage rows w*ROWS/4 + 8i + lane/8 (x rows first, then
+    // plane rows p*32 + e of expert tile et); chunk (lane%8) ^ rswz(row)
+    const uint16_t* src[CI];
 #pragma unroll
-    for (int j = 0; j < RV_NGMAX; ++j) {
-        gsc[j] = -INFINITY;
-        if (j < NG) {
-            float b1 = -INFINITY, b2 = -INFINITY;
-            for (int e0 = j * G; e0 < (j + 1) * G; e0 += 4) {
-                const int e = e0 + 2 * u;
-                const float2 v2 = *reinterpret_cast<const float2*>(srow + e);
-                const float2 bb = *reinterpret_cast<const float2*>(s_bias + e);
-                const float c0 = v2.x + bb.x;
-                const float c1 = v2.y + bb.y;
-                b2 = fmaxf(b2, fminf(b1, c0));
-                b1 = fmaxf(b1, c0);
-                b2 = fmaxf(b2, fminf(b1, c1));
-                b1 = fmaxf(b1, c1);
+    for (int i = 0; i < CI; ++i) {
+        const int r = wave * (ROWS / 4) + i * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ rswz(r);
+        if (r < TOK) {
+            int64_t t = t0 + r;
+            if (t >= a.T) t = a.T - 1;
+            src[i] = a.x + t * H + c * 8;
+        } else {
+            const int q = r - TOK, p = q / 32;
+            int e = et * 32 + q % 32;
+            if (e >= E) e = E - 1;
+            src[i] = a.planes + (static_cast<int64_t>(p) * E + e) * H + c * 8;
+        }
+    }
+    auto issue = [&](int kt, int s) {
+        const uint32_t base = lds_addr(smem + s * STAGE + wave * (ROWS / 4) * BK);
+#pragma unroll
+        for (int i = 0; i < CI; ++i) lds_dma16(src[i] + kt * BK, base + i * 8 * BK * 2);
+    };
+    const int kh = lane >> 5, rl = lane & 31;
+    f32x16 acc = f32x16{};
+    if (kt0 < kt1) issue(kt0, 0);
+    for (int kt = kt0; kt < kt1; ++kt) {
+        const int s = (kt - kt0) & 1;
+        wait_vmcnt<0>();
+        wait_lgkmcnt0();
+        block_barrier();                                // k-tile kt landed; stage 1 - s free
+        if (kt + 1 < kt1) issue(kt + 1, 1 - s);
+        const uint16_t* st = smem + s * STAGE;
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            const int ch = kk * 2 + kh;
+            const int rx = wave * 32 + rl;
+            const bf16x8 xf = *reinterpret_cast<const bf16x8*>(st + rx * BK + ((ch ^ rswz(rx)) * 8));
+#pragma unroll
+            for (int p = 0; p < 3; ++p) {
+                const int rw = TOK + p * 32 + rl;
+                const bf16x8 wf = *reinterpret_cast<const bf16x8*>(st + rw * BK + ((ch ^ rswz(rw)) * 8));
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, xf, acc, 0, 0, 0);
             }
-            const float p1 = __shfl_xor(b1, 1), p2 = __shfl_xor(b2, 1);
-            gsc[j] = fmaxf(b1, p1) + fmaxf(fminf(b1, p1), fmaxf(b2, p2));
         }
     }
-    // kept groups: repeated arg-max, lower index on ties; then their indices ascending
-    uint32_t kept = 0;
-    for (int r = 0; r < a.TG; ++r) {
-        float bv = -INFINITY;
-        int bj = -1;
+    // lane holds experts et*32 + 8q + 4*kh + [0, 4) of token t0 + 32 w + rl
+    const int64_t t = t0 + wave * 32 + rl;
+    if (t < a.T) {
+        float* zrow = zpart + (static_cast<int64_t>(part) * a.T + t) * EP + et * 32;
 #pragma unroll
-        for (int j = 0; j < RV_NGMAX; ++j) {
-            const bool take = j < NG && !((kept >> j) & 1u) && (bj < 0 || gsc[j] > bv);
-            bv = take ? gsc[j] : bv;
-            bj = take ? j : bj;
-        }
-        kept |= 1u << bj;
+        for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<float4*>(zrow + 8 * q + 4 * kh) =
+                make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
     }
-    // top-K (first KMAX) in (c descending, id ascending) order, as 64-bit
-    // keys: an order-preserving image of c (with -0 taken as +0) above the
-    // complement of the id, so that the larger key is the larger c, or the
-    // lower id on equal c.  A sorted insertion is then
-    // key[k] = max(key[k], min(key[k-1], new)).  Each lane inserts its half
-    // of the kept groups' experts, then the partner's list.
-    auto okey = [](float c, int e) -> uint64_t {
-        uint32_t b = __float_as_uint(c + 0.0f);
-        b ^= static_cast<uint32_t>(static_cast<int32_t>(b) >> 31) | 0x80000000u;
-        return (static_cast<uint64_t>(b) << 32) | static_cast<uint32_t>(~e);
-    };
-    uint64_t key[KMAX];
+}
+
+// grid: ceil(T / 4); 4 waves, one token each: the parts of the logits added
+// in a fixed order, then scores and routing by the wave.
+__global__ __launch_bounds__(256) void route_select_kernel(RouteV2Args a, const float* zpart,
+                                                           int EP, int EPL, int LG) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (t >= a.T) return;
+    const int e0 = lane * EPL;
+    float s[4], c[4];
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) key[k] = 0;           // below every real key; decodes to id -1
-    auto insert = [&](uint64_t nk) {
+    for (int q = 0; q < 4; ++q) {
+        s[q] = 0.f;
+        c[q] = -INFINITY;
+        const int e = e0 + q;
+        if (q < EPL && e < a.E) {
+            float z = 0.f;
 #pragma unroll
-        for (int k = KMAX - 1; k > 0; --k) {
-            const uint64_t lo = key[k - 1] < nk ? key[k - 1] : nk;
-            key[k] = key[k] > lo ? key[k] : lo;
-        }
-        key[0] = key[0] > nk ? key[0] : nk;
-    };
-    uint32_t rem = kept;
-    for (int r = 0; r < a.TG; ++r) {
-        const int j = __builtin_ctz(rem);
-        rem &= rem - 1;
-        for (int e0 = j * G; e0 < (j + 1) * G; e0 += 4) {
-            const int e = e0 + 2 * u;
-            const float2 v2 = *reinterpret_cast<const float2*>(srow + e);
-            const float2 bb = *reinterpret_cast<const float2*>(s_bias + e);
-            insert(okey(v2.x + bb.x, e));
-            insert(okey(v2.y + bb.y, e + 1));
+            for (int pp = 0; pp < RS_SPLIT; ++pp) z += zpart[(static_cast<int64_t>(pp) * a.T + t) * EP + e];
+            s[q] = 1.0f / (1.0f + expf(-z));
+            c[q] = s[q] + a.bias[e];
         }
     }
-    {
-        uint64_t pk[KMAX];
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k) {
-            const uint32_t hi = __shfl_xor(static_cast<uint32_t>(key[k] >> 32), 1);
-            const uint32_t lo = __shfl_xor(static_cast<uint32_t>(key[k]), 1);
-            pk[k] = (static_cast<uint64_t>(hi) << 32) | lo;
-        }
-#pragma unroll
-        for (int m = 0; m < KMAX; ++m) insert(pk[m]);
-    }
-    int id[KMAX];
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k) id[k] = static_cast<int>(~static_cast<uint32_t>(key[k]));
-    // weights from the raw scores, slot order sum, scaled once; lane u stores
-    // the slots k with k % 2 == u
     const bool valid = a.mask == nullptr || a.mask[t] != 0;
-    float sk[KMAX];
-    float sum = 0.f;
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-        sk[k] = 0.f;
-        if (k < a.K) {
-            sk[k] = srow[id[k]];
-            sum += sk[k];
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-        if (k < a.K && (k & 1) == u) {
-            float wv = a.norm ? sk[k] / sum : sk[k];
-            wv = wv * a.rsf;
-            a.ids[t * a.K + k] = valid ? id[k] : -1;
-            a.w[t * a.K + k] = valid ? wv : 0.f;
-        }
-    }
+    wave_route(t, lane, a.E, EPL, LG, a.G, a.NG, a.TG, a.K, a.norm, a.rsf, valid, s, c, a.ids, a.w);
 }
 
 }  // namespace
@@ -655,8 +790,15 @@ bool route_bf16_path(const Dims& d) {
     return d.bf16 && d.E <= 128 && d.NG <= RV_NGMAX && d.G % 4 == 0;
 }
 
+// planes of W_r, then the partial logits of the few-token path
+static size_t route_planes_bytes(const Dims& d) {
+    return (static_cast<size_t>(3) * d.E * d.H * sizeof(uint16_t) + 255) / 256 * 256;
+}
+
 size_t route_ws_bytes(const Dims& d) {
-    return route_bf16_path(d) ? static_cast<size_t>(3) * d.E * d.H * sizeof(uint16_t) : 0;
+    if (!route_bf16_path(d)) return 0;
+    const int EP = d.E <= 64 ? 64 : 128;
+    return route_planes_bytes(d) + static_cast<size_t>(RS_SPLIT) * RS_TMAX * EP * sizeof(float);
 }
 
 hipError_t launch_route(const Dims& d, const void* x, const float* router_w, const float* e_bias,
@@ -685,6 +827,19 @@ hipError_t launch_route(const Dims& d, const void* x, const float* router_w, con
         a.G = d.G;
         a.norm = d.norm;
         a.rsf = d.rsf;
+        if (d.T <= RS_TMAX) {
+            // few tokens: hidden-dimension split, then a scoring and routing pass
+            float* zpart = reinterpret_cast<float*>(static_cast<char*>(ws) + route_planes_bytes(d));
+            const unsigned nt = static_cast<unsigned>((d.T + 127) / 128);   // logits: 128-token tiles
+            const int EP = d.E <= 64 ? 64 : 128;
+            if (EP == 64)
+                hipLaunchKernelGGL(route_logits_kernel<64>, dim3(nt, 2, RS_SPLIT), dim3(256), 0, stream, a, zpart);
+            else
+                hipLaunchKernelGGL(route_logits_kernel<128>, dim3(nt, 4, RS_SPLIT), dim3(256), 0, stream, a, zpart);
+            hipLaunchKernelGGL(route_select_kernel, dim3(static_cast<unsigned>((d.T + 3) / 4)), dim3(256), 0,
+                               stream, a, zpart, EP, d.EPL, d.LG);
+            return hipGetLastError();
+        }
         // tokens per workgroup: the fewest (32 TM, TM = 4..6) whose grid fits
         // in one round over the CUs, else the most
         const int ncu = cu_count();

@@ -127,7 +127,9 @@ def test_route_validation_paths():
     c = lbv.config()
     L = raw()
     need = lbv.lbv_moe_route_workspace_size(c)
-    assert need == 3 * 128 * 2048 * 2                    # three bf16 planes of W_r
+    # three bf16 planes of W_r, then partial logits of the few-token path
+    # (4 hidden-dimension parts x 4096 tokens x 128 experts, fp32)
+    assert need == 3 * 128 * 2048 * 2 + 4 * 4096 * 128 * 4
 
     def r(T, x, wr, b, ids, w, ws=Cc, nbytes=need):
         return L.lbv_moe_route(ctypes.byref(c), T, x, wr, b, None, ids, w, ws, nbytes, None)
