@@ -20,7 +20,8 @@
 // MFMAs while the other waits.  A and B tiles (K-contiguous, BK = 64 bf16 =
 // 128 B per row, so every copy instruction moves whole 128-byte lines) go
 // straight from global memory to LDS with global_load_lds_dwordx4 into two
-// stages.  Waves 0-3 (one per SIMD) issue the copies of the next k-tile one
+// stages (three for the 64-row tiles used when segments hold few rows).
+// Waves 0-3 (one per SIMD) issue the copies of the next k-tile one
 // at a time between their MFMAs of the current one (a burst of copies stalls
 // the issuing wave until the address unit takes them); the LDS reads of
 // slice g + 1 sit between the MFMAs of slice g; one barrier per k-tile hands a
@@ -36,9 +37,9 @@
 #include "lbv_internal.h"
 #include "lbv_pipe.h"
 
-// Compile-time shape of the bf16 path: workgroup tile BM x BN (2 x 2 waves;
-// the gate/up GEMM's BN counts gate and up rows together, BN/2 act columns
-// per tile); NPRE: MFMAs of a k-tile's last slice issued before its barrier;
+// Compile-time shape of the bf16 path: workgroup tile BM x BN (the gate/up
+// GEMM's BN counts gate and up rows together, BN/2 act columns per tile);
+// NPRE: MFMAs of a k-tile's last slice issued before its barrier;
 // COPY_SLICES: slices of a k-tile that carry the next k-tile's copies;
 // EPI_NT: non-temporal output stores (act and y are written once and not
 // reread while the matmul runs, so they need not displace operand lines);
@@ -47,10 +48,8 @@
 // G*_WAVES: waves per workgroup (4 or 8); G*_COPY_WAVES: waves that issue
 // the stage copies; G*_ORDER: m-tiles per block of the tile order (1: m-tile
 // major, the n-tiles of an m-tile adjacent; large: n-tile major inside each
-// segment).
-#ifndef LBV_MFMA_FENCE
-#define LBV_MFMA_FENCE 1
-#endif
+// segment); FEW_ROWS / FEW_STAGES: below FEW_ROWS rows per segment on average
+// the matmuls use 64-row tiles with a FEW_STAGES-deep ring.
 #ifndef LBV_NPRE
 #define LBV_NPRE 8
 #endif
@@ -115,7 +114,7 @@ struct GemmArgs {
     const void* B;          // gate/up: w13 [E, 2I, H];  down: w2 [E, H, I]
     const void* Bsh;        // gate/up: shared_w13 [2 Is, H];  down: shared_w2 [H, Is]
     const int32_t* offsets; // [S + 1]
-    const int32_t* rows;    // gate/up: sorted_rows (slot ids)
+    const int32_t* rows;    // sorted_rows: slot id of each sorted row
     void* C;                // gate/up: act [rows, I];  down: y [rows, H]
     int64_t T;
     int H, I, E, NS, KS, S;
@@ -186,12 +185,12 @@ constexpr int kMaxSeg = 512;
 
 // Persistent bf16 grouped matmul.  The grid is a multiple of 8 workgroups, one
 // per CU; workgroup b serves XCD b % 8, which owns a contiguous eighth of the
-// logical tiles (m-tile major, ntn n-tiles per m-tile), handed to its
-// workgroups round-robin, so the tiles in flight on one XCD share operand rows
-// in its L2.  Each workgroup builds the segment tile table once, then runs
-// one continuous k-loop over all its tiles: the copies of the next tile's
-// first k-tile are issued during the current tile's last k-tile and land
-// while its epilogue runs.
+// logical tiles (ordered segment by segment, inside a segment by ORDER),
+// handed to its workgroups round-robin, so the tiles in flight on one XCD
+// share operand rows in its L2.  Each workgroup builds the segment tile table
+// once, then runs one continuous k-loop over all its tiles: the copies of the
+// next tile's first STG-1 k-tiles are issued during the current tile's last
+// k-tiles and land while its epilogue runs.
 template <int BM, int BN, int MODE, int NW, int CWV, int ORDER, int STG>
 __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     // NW waves: 2 along the tokens x NW/2 along the weight rows (NW = 4: one
@@ -294,15 +293,15 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     };
 
     // ---- copy sources: a wave-uniform base (scalar registers, advanced by BK
-    // per k-tile) plus a 32-bit per-lane byte offset.  Instruction i of wave w
-    // fills LDS rows w*(rows/4) + RPI i + [0, RPI) of a stage; lane l lands at
-    // row +l/CPR, physical chunk l%CPR, which holds logical chunk
-    // (l%CPR) ^ swz(row). ---------------------------------------------------------
+    // per k-tile) plus a 32-bit per-lane byte offset.  Instruction i of
+    // copying wave w fills LDS rows w*(rows/CW) + RPI i + [0, RPI) of a stage's
+    // A or B part; lane l lands at row +l/CPR, physical chunk l%CPR, which
+    // holds logical chunk (l%CPR) ^ swz(row). ---------------------------------------
     const uint16_t* abase;
     const uint16_t* bbase;
     uint32_t aoff[AI], boff[BI];
-    // Slot ids of a tile's BM rows, copied into s_rid by waves 0..3, 64 rows
-    // each (a copy like the stage copies, counted by the same waits).  The
+    // Slot ids of a tile's BM rows, copied into s_rid by waves 0 .. BM/64-1,
+    // 64 rows each (a copy like the stage copies, counted by the same waits).  The
     // gate/up matmul gathers its x rows by them; the down matmul stores its
     // output rows to them.
     auto rid_copy = [&](int seg_r0_, int seg_n_, int m0_) {
@@ -503,7 +502,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
                     copy_one(TS, KF, d);                                                       \
             }                                                                                  \
         }                                                                                      \
-        if (LBV_MFMA_FENCE) __builtin_amdgcn_sched_barrier(0);                                 \
+        __builtin_amdgcn_sched_barrier(0);                                                     \
     }
 
     // Next tile (valid when has_next): its lookup is done at the start of the
