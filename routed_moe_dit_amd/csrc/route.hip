@@ -9,19 +9,24 @@
 //   weight = s at those experts (no bias), normalised over the chosen experts
 //   when norm_topk_prob, times routed_scaling_factor, once.
 //
-// Design:
-//  * One workgroup (4 waves) routes 64 tokens.  The logits of the 64 tokens
-//    against all experts are an fp32 matrix product done with
-//    v_mfma_f32_32x32x2_f32 (exact fp32 products, fp32 accumulation) on
-//    32-wide hidden chunks of x and W_r staged through LDS.  bf16 x is
-//    widened exactly to fp32 when staged.
-//  * The logits go to LDS; then each wave routes one token at a time with its
-//    64 lanes: lane l owns experts [l*EPL, (l+1)*EPL).  A group then occupies
-//    LG = G/EPL neighbouring lanes (16 lanes, one DPP row, for E=128), so the
-//    in-group top-2 is a butterfly over LG lanes.  Group choice and expert
-//    choice are repeated wave-wide arg-max reductions on 64-bit keys
-//    (order-preserving score bits, inverted index), so ties go to the lower
-//    index exactly as in a sequential scan.
+// Three paths:
+//  * bf16 x, E <= 128 (the block's configuration), more than 4096 tokens:
+//    route_bf16_kernel computes the fp32 logits on the bf16 matrix cores from
+//    an exact three-plane split of W_r, then routes two lanes per token (see
+//    the comment above it).
+//  * bf16 x, E <= 128, at most 4096 tokens: route_logits_kernel splits the
+//    same product along the hidden dimension over more workgroups and
+//    route_select_kernel adds the parts and routes one token per wave.
+//  * otherwise (fp32 x, more experts or groups): route_kernel, one workgroup
+//    (4 waves) per 64 tokens, logits with v_mfma_f32_32x32x2_f32 on 32-wide
+//    hidden chunks of x and W_r staged through LDS (bf16 x widened exactly),
+//    then one token per wave.
+// Wave-per-token routing (wave_route): lane l owns experts [l*EPL,
+// (l+1)*EPL); a group occupies LG = G/EPL neighbouring lanes, so the in-group
+// top-2 is a butterfly over LG lanes.  Group choice and expert choice are
+// repeated wave-wide arg-max reductions on 64-bit keys (order-preserving
+// score bits, inverted index), so ties go to the lower index exactly as in a
+// sequential scan.
 #include "lbv_internal.h"
 #include "lbv_pipe.h"
 
