@@ -47,6 +47,11 @@ ROUTE_CASES = [
         dtype="f32"),
     var("E16_plain_T1", num_experts=16, n_group=1, topk_group=1, top_k=5, T=1, hidden=64),
     var("nonorm_negbias", norm_topk_prob=False, b_std=1.0, T=130),
+    # above and below the 4096-token switch between the one-pass router and
+    # the hidden-split router, for 64 experts and for top_k > 8
+    var("E64_T5000", num_experts=64, n_group=4, topk_group=2, top_k=6, T=5000, hidden=256),
+    var("E128_K12_T300", num_experts=128, n_group=4, topk_group=2, top_k=12, T=300, hidden=256),
+    var("E128_K12_T5000", num_experts=128, n_group=4, topk_group=2, top_k=12, T=5000, hidden=256),
 ]
 
 
