@@ -247,6 +247,7 @@ FWD_CASES = [
     var("nonorm", norm_topk_prob=False, T=60),
     var("T1", T=1),
     var("f32_ragged", dtype="f32", T=45, hidden=128, intermediate=64),
+    var("E128_K12_ns2", num_experts=128, top_k=12, n_shared=2, T=300, hidden=256),
 ]
 
 
@@ -273,6 +274,19 @@ def test_forward_parity(wl):
     d = upload(wl, inp)
     out, ids, w = forward(wl, d)
     check_forward(wl, inp, out, ids, w)
+
+
+def test_forward_parity_mid_size():
+    """6,000 tokens (past the router's 4096-token switch, 256-row matmul
+    tiles): 64 sampled tokens against the oracle."""
+    wl = var("E128_T6000", num_experts=128, top_k=8, T=6000, hidden=256, intermediate=256)
+    note("forward %s" % wl.name)
+    inp = synth.make_inputs(wl)
+    d = upload(wl, inp)
+    out, ids, w = forward(wl, d)
+    rows = np.unique(np.concatenate([np.random.default_rng(7).choice(wl.T, 62, replace=False),
+                                     [0, wl.T - 1]]))
+    check_forward(wl, inp, out, ids, w, rows)
 
 
 def test_forward_parity_padded_batch():
