@@ -41,7 +41,7 @@
 // GEMM's BN counts gate and up rows together, BN/2 act columns per tile);
 // NPRE: MFMAs of a k-tile's last slice issued before its barrier;
 // COPY_SLICES: slices of a k-tile that carry the next k-tile's copies;
-// EPI_NT: non-temporal output stores (act and y are written once and not
+// G*_EPI_NT: non-temporal output stores (act and y are written once and not
 // reread while the matmul runs, so they need not displace operand lines);
 // COMB_CHUNKS / COMB_NT: 16-byte chunks per lane per combine step, and
 // non-temporal combine loads;
@@ -74,8 +74,11 @@
 #ifndef LBV_COMB_NT
 #define LBV_COMB_NT 1
 #endif
-#ifndef LBV_EPI_NT
-#define LBV_EPI_NT 1
+#ifndef LBV_G1_EPI_NT
+#define LBV_G1_EPI_NT 1
+#endif
+#ifndef LBV_G2_EPI_NT
+#define LBV_G2_EPI_NT 1
 #endif
 #ifndef LBV_G1_ORDER
 #define LBV_G1_ORDER 1
@@ -661,7 +664,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
                 const int64_t orow = MODE == 0 ? seg_r0 + m : s_rid[wm * (BM / 2) + p * PROWS + row];
                 if (m < seg_n && col < ncols) {
                     u32x4* dst = reinterpret_cast<u32x4*>(C + orow * ncols + col);
-                    if (LBV_EPI_NT) __builtin_nontemporal_store(v, dst);
+                    if (MODE == 0 ? LBV_G1_EPI_NT : LBV_G2_EPI_NT) __builtin_nontemporal_store(v, dst);
                     else *dst = v;
                 }
             }
