@@ -72,6 +72,12 @@ def lib():
         L.orc_shared_act.restype = None
         L.orc_expert_out.argtypes = [P, P, P, P, ctypes.c_int, P]
         L.orc_expert_out.restype = None
+        L.orc_moe_forward_ids.argtypes = [P, ctypes.c_int64, P, P, P, P, P, P, P, P, P]
+        L.orc_moe_forward_ids.restype = ctypes.c_int
+        L.orc_act_rows.argtypes = [P, ctypes.c_int64, P, P, P, P, P, P]
+        L.orc_act_rows.restype = None
+        L.orc_down_combine.argtypes = [P, ctypes.c_int64, P, P, P, P, P, P]
+        L.orc_down_combine.restype = None
         _lib = L
     return _lib
 
@@ -138,6 +144,57 @@ def moe_forward(wl, x, router_w, e_bias, w13, w2, shared_w13=None, shared_w2=Non
     if rc != 0:
         raise ValueError("oracle: invalid routing configuration")
     return dict(out=out, ids=ids, w=w, m_grp=mg, m_sel=ms)
+
+
+def moe_forward_ids(wl, x, router_w, ids, w13, w2, shared_w13=None, shared_w2=None):
+    """Block output for a given expert choice ids [n, K] (entries outside [0, E)
+    are empty slots): the oracle's own scores, weights at the given ids.
+    Returns dict(out fp64 [n, H], w fp32 [n, K])."""
+    x, router_w = _f32(x), _f32(router_w)
+    w13, w2 = _f32(w13), _f32(w2)
+    shared_w13, shared_w2 = _f32(shared_w13), _f32(shared_w2)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    n, K, H = x.shape[0], wl.top_k, wl.hidden
+    assert ids.shape == (n, K)
+    assert w13.shape == (wl.num_experts, 2 * wl.intermediate, H)
+    out = np.empty((n, H), np.float64)
+    w = np.empty((n, K), np.float32)
+    c = cfg_of(wl)
+    rc = lib().orc_moe_forward_ids(ctypes.byref(c), n, _p(x), _p(router_w), _p(ids), _p(w13),
+                                   _p(w2), _p(shared_w13), _p(shared_w2), _p(out), _p(w))
+    if rc != 0:
+        raise ValueError("oracle: invalid configuration")
+    return dict(out=out, w=w)
+
+
+def act_rows(wl, x, w13, shared_w13, tok, seg):
+    """fp64 act [n, I] for (token, segment) pairs; segment E + j is the j-th
+    width-I slice of the shared MLP."""
+    x, w13, shared_w13 = _f32(x), _f32(w13), _f32(shared_w13)
+    tok = np.ascontiguousarray(tok, dtype=np.int32)
+    seg = np.ascontiguousarray(seg, dtype=np.int32)
+    assert tok.shape == seg.shape and tok.ndim == 1
+    assert tok.size == 0 or (tok.min() >= 0 and tok.max() < x.shape[0])
+    assert seg.size == 0 or (seg.min() >= 0 and seg.max() < wl.num_experts + wl.n_shared)
+    act = np.empty((tok.size, wl.intermediate), np.float64)
+    c = cfg_of(wl)
+    lib().orc_act_rows(ctypes.byref(c), tok.size, _p(x), _p(w13), _p(shared_w13), _p(tok),
+                       _p(seg), _p(act))
+    return act
+
+
+def down_combine(wl, act_slots, ids, w, w2, shared_w2=None):
+    """out [n, H] fp64 from given act vectors per slot: act_slots [n, K+ns, I]."""
+    act_slots, w2, shared_w2 = _f32(act_slots), _f32(w2), _f32(shared_w2)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    w = _f32(w)
+    n, K, KS = ids.shape[0], wl.top_k, wl.top_k + wl.n_shared
+    assert act_slots.shape == (n, KS, wl.intermediate) and w.shape == (n, K)
+    out = np.empty((n, wl.hidden), np.float64)
+    c = cfg_of(wl)
+    lib().orc_down_combine(ctypes.byref(c), n, _p(act_slots), _p(ids), _p(w), _p(w2),
+                           _p(shared_w2), _p(out))
+    return out
 
 
 def expert_act(wl, x_row, w13, e):

@@ -310,6 +310,129 @@ int orc_moe_forward(const orc_cfg *c, int64_t ntok, const float *x, const uint8_
 }
 
 /*
+ * Route with a given expert choice.  The scores s come from the oracle's own
+ * router (steps above); the chosen experts are taken from ids_in [ntok, K]
+ * instead of the group-limited top-k (an id outside [0, E) is an empty slot).
+ * The weights follow the same rule as route_one on that choice: raw scores at
+ * the given ids, summed in slot order, divided by the sum when
+ * norm_topk_prob, times the routed scaling factor once; empty slots weigh 0.
+ * The output is the block output for that choice (same expert MLPs and the
+ * same combine as orc_moe_forward), so a token on which a kernel made another
+ * near-equal choice can still be compared element by element.
+ * out [ntok, H] fp64; w_out [ntok, K] fp32.
+ */
+int orc_moe_forward_ids(const orc_cfg *c, int64_t ntok, const float *x, const float *wr,
+                        const int32_t *ids_in, const float *w13, const float *w2,
+                        const float *shared_w13, const float *shared_w2, double *out,
+                        float *w_out)
+{
+    const int H = c->hidden, K = c->top_k, I = c->intermediate, E = c->num_experts;
+    const int Is = c->intermediate * c->n_shared;
+    if (E <= 0 || K <= 0) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < ntok; ++t) {
+        const float *xt = x + t * H;
+        const int32_t *it = ids_in + t * K;
+        float *wt = w_out + t * K;
+        double *ot = out + t * H;
+        float *z = (float *)malloc(sizeof(float) * E);
+        router_logits(H, E, xt, wr, z);
+        float sum = 0.0f;
+        for (int k = 0; k < K; ++k) {
+            if (it[k] < 0 || it[k] >= E) continue;
+            sum += 1.0f / (1.0f + expf(-z[it[k]]));
+        }
+        for (int k = 0; k < K; ++k) {
+            if (it[k] < 0 || it[k] >= E) { wt[k] = 0.0f; continue; }
+            float v = 1.0f / (1.0f + expf(-z[it[k]]));
+            if (c->norm_topk_prob) v = v / sum;
+            wt[k] = v * c->routed_scaling_factor;
+        }
+        free(z);
+        int wmax = I > Is ? I : Is;
+        double *act = (double *)malloc(sizeof(double) * (wmax > 0 ? wmax : 1));
+        double *y = (double *)malloc(sizeof(double) * H);
+        for (int n = 0; n < H; ++n) ot[n] = 0.0;
+        for (int k = 0; k < K; ++k) {
+            if (it[k] < 0 || it[k] >= E) continue;
+            swiglu_act(H, I, I, xt, w13 + (size_t)it[k] * 2 * I * H, act);
+            down_proj(H, I, I, w2 + (size_t)it[k] * H * I, act, y);
+            for (int n = 0; n < H; ++n) ot[n] += (double)wt[k] * y[n];
+        }
+        if (Is > 0 && shared_w13 && shared_w2) {
+            swiglu_act(H, Is, Is, xt, shared_w13, act);
+            down_proj(H, Is, Is, shared_w2, act, y);
+            for (int n = 0; n < H; ++n) ot[n] += y[n];
+        }
+        free(act);
+        free(y);
+    }
+    return 0;
+}
+
+/*
+ * act rows of the gate/up stage for n (token, segment) pairs: segment s < E is
+ * routed expert s, segment E + j the j-th width-I slice of the shared MLP
+ * (gate rows jI .. jI+I-1 and up rows I_s + jI .. of shared_w13).
+ * act[r, i] = silu(gate_i . x[tok[r]]) * (up_i . x[tok[r]]), fp64.
+ * act [n, I].
+ */
+void orc_act_rows(const orc_cfg *c, int64_t n, const float *x, const float *w13,
+                  const float *shared_w13, const int32_t *tok, const int32_t *seg, double *act)
+{
+    const int H = c->hidden, I = c->intermediate, E = c->num_experts;
+    const long Is = (long)c->intermediate * c->n_shared;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t r = 0; r < n; ++r) {
+        const float *xt = x + (size_t)tok[r] * H;
+        if (seg[r] < E) {
+            swiglu_act(H, I, I, xt, w13 + (size_t)seg[r] * 2 * I * H, act + r * I);
+        } else {
+            const long j = seg[r] - E;
+            /* gate rows start at j*I, up rows at I_s + j*I: offset between them I_s */
+            swiglu_act(H, I, Is, xt, shared_w13 + (size_t)j * I * H, act + r * I);
+        }
+    }
+}
+
+/*
+ * Down projection and weighted combine from given act values, per token:
+ *   out[t] = sum_{k < K, ids[t,k] in [0,E)} w[t,k] * W2[ids[t,k]] act[t,k]
+ *          + sum_{j < n_shared} W2_shared[:, jI:(j+1)I] act[t, K+j]
+ * act [ntok, K + n_shared, I] (the act vector of each slot), ids/w [ntok, K],
+ * w2 [E, H, I], shared_w2 [H, I_s]; out [ntok, H] fp64.
+ */
+void orc_down_combine(const orc_cfg *c, int64_t ntok, const float *act, const int32_t *ids,
+                      const float *w, const float *w2, const float *shared_w2, double *out)
+{
+    const int H = c->hidden, I = c->intermediate, E = c->num_experts, K = c->top_k;
+    const int NS = c->n_shared, KS = K + NS;
+    const long Is = (long)I * NS;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t t = 0; t < ntok; ++t) {
+        double *ot = out + t * H;
+        double *a = (double *)malloc(sizeof(double) * I);
+        double *y = (double *)malloc(sizeof(double) * H);
+        for (int n = 0; n < H; ++n) ot[n] = 0.0;
+        for (int k = 0; k < KS; ++k) {
+            const float *ak = act + ((size_t)t * KS + k) * I;
+            for (int i = 0; i < I; ++i) a[i] = ak[i];
+            if (k < K) {
+                const int e = ids[t * K + k];
+                if (e < 0 || e >= E) continue;
+                down_proj(H, I, I, w2 + (size_t)e * H * I, a, y);
+                for (int n = 0; n < H; ++n) ot[n] += (double)w[t * K + k] * y[n];
+            } else {
+                down_proj(H, I, Is, shared_w2 + (size_t)(k - K) * I, a, y);
+                for (int n = 0; n < H; ++n) ot[n] += y[n];
+            }
+        }
+        free(a);
+        free(y);
+    }
+}
+
+/*
  * Token copies sorted by expert ([P2] "MoE 实现的源码级要点": tokens are
  * reordered by expert before the grouped matmuls and restored after).
  * Plain stable counting sort of the slots by segment.  Slot (t, k), k < K, is
