@@ -4,15 +4,25 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one lbv_moe_forward (router, permutation, gate/up GEMM with SiLU,
 down GEMM, weighted combine) over the workload's tokens, inputs resident in
-HBM.  Prints one JSON line: MoE-layer tokens/s over K timed steps, the
-grouped-GEMM TFLOP/s and its fraction of the bf16 MFMA peak, a roofline
-object for the dominant kernel (the gate/up GEMM) timed with events around
-its own launches on the launch stream, and the CPU oracle timed on a bounded
-token sample on the host.
+HBM.  Prints one JSON line:
+  * MoE-layer tokens/s over K timed steps (one event before the first step
+    and one after each step, so the per-step median / p10 / p90 come from the
+    same region);
+  * the grouped-GEMM TFLOP/s: the algorithmic FLOPs of both grouped matmuls
+    (routed + shared) over the summed time of lbv_moe_gemm_w13_silu and
+    lbv_moe_gemm_w2_combine, and its fraction of the bf16 MFMA peak;
+  * stage times of the four split calls (events on the launch stream);
+  * a roofline object for the dominant kernel, the gate/up GEMM: bound by
+    HBM when its algorithmic FLOP per byte is below the machine balance (few
+    tokens: the weights stream once), else by the bf16 matrix cores;
+  * router and permutation rates, the input digests, and the CPU oracle timed
+    on a bounded token sample on the host.
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -22,15 +32,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-HBM_PEAK_GBS = 8000.0
-
-# Bytes the gate/up GEMM moves between L2 and memory per launch on
-# default_gen_T38000: rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch,
-# two --pmc runs of `bench.py --copy-calibration`), each scaled by what the same
-# counter reads for a plain 1 GiB device copy (FETCH_SIZE x 2.000, WRITE_SIZE
-# x 1.000): 3,297,198 KiB x 2 read + 556,954 KiB written.  Re-measure whenever
-# the kernel changes (None then).
-GEMM_W13_TRAFFIC_BYTES = 7.3228e9
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+KERNEL_SOURCES = ("routed_moe_dit_amd/csrc/gemm.hip", "routed_moe_dit_amd/csrc/lbv_pipe.h",
+                  "routed_moe_dit_amd/csrc/lbv_internal.h")
 
 
 def parse():
@@ -39,13 +44,56 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="default_gen_T38000")
-    p.add_argument("--cpu-sample", type=int, default=8192,
+    p.add_argument("--cpu-sample", type=int, default=12000,
                    help="tokens of the same workload the CPU oracle is timed on")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after the measurements, run a plain 1 GiB device copy three times, so "
                         "that a hardware-counter run can scale its byte counters")
     return p.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload, kernel):
+    """Bytes per launch from a counter summary in profiles/ (a JSON block with
+    the kernel, the workload and the hash of the kernel sources it was taken
+    on); None when there is none for the current sources."""
+    d = os.path.join(ROOT, "profiles")
+    want = kernel_source_hash()
+    for name in sorted(os.listdir(d)) if os.path.isdir(d) else []:
+        if not name.endswith(".md"):
+            continue
+        text = open(os.path.join(d, name)).read()
+        for block in re.findall(r"```json\n(.*?)\n```", text, flags=re.S):
+            try:
+                rec = json.loads(block)
+            except ValueError:
+                continue
+            if (rec.get("kind") == "traffic" and rec.get("workload") == workload and
+                    rec.get("kernel") == kernel and rec.get("source_sha256") == want):
+                return float(rec["read_bytes"]) + float(rec["write_bytes"])
+    return None
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def pct(a, q):
+    return float(np.percentile(np.asarray(a, np.float64), q))
 
 
 def main():
@@ -66,6 +114,7 @@ def main():
     t_gen = time.time()
     inp = synth.make_inputs(wl)
     t_gen = time.time() - t_gen
+    digests = synth.digest(inp)
 
     def dev(a, bf):
         if a is None:
@@ -75,6 +124,7 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
     bf = wl.dtype == "bf16"
+    esz = 2 if bf else 4
     x = dev(inp["x"], bf)
     router_w, e_bias = dev(inp["router_w"], False), dev(inp["e_bias"], False)
     w13, w2 = dev(inp["w13"], bf), dev(inp["w2"], bf)
@@ -96,19 +146,20 @@ def main():
         lbv.lbv_moe_forward(cfg, x, mask, router_w, e_bias, w13, w2, sw13, sw2, out, ids, wts, ws,
                             stream)
 
-    # ---- whole-block throughput ------------------------------------------------
+    # ---- whole-block throughput: K steps, an event after each ---------------------
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for i in range(args.steps):
         step()
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = evs[0].elapsed_time(evs[-1]) / args.steps
+    per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
 
     # ---- per-stage timing with the split calls on the same stream ------------------
     off = torch.empty(S + 1, dtype=torch.int32, device="cuda")
@@ -118,22 +169,23 @@ def main():
                       device="cuda")
     act = torch.empty(T * KS, I, dtype=x.dtype, device="cuda")
     yws = torch.empty(lbv.lbv_moe_w2_workspace_size(cfg, T), dtype=torch.uint8, device="cuda")
+    gws = torch.empty(lbv.lbv_moe_w13_workspace_size(cfg, T), dtype=torch.uint8, device="cuda")
     rws = torch.empty(max(lbv.lbv_moe_route_workspace_size(cfg), 16), dtype=torch.uint8,
                       device="cuda")
     stages = ["route", "permute", "gemm_w13_silu", "gemm_w2_combine"]
 
-    def split(evs):
-        evs[0].record(stream)
+    def split(evs_):
+        evs_[0].record(stream)
         lbv.lbv_moe_route(cfg, x, router_w, e_bias, mask, ids, wts, rws, stream)
-        evs[1].record(stream)
+        evs_[1].record(stream)
         lbv.lbv_moe_permute(cfg, ids, off, srt, inv, pws, stream)
-        evs[2].record(stream)
-        lbv.lbv_moe_gemm_w13_silu(cfg, x, w13, sw13, off, srt, act, stream)
-        evs[3].record(stream)
+        evs_[2].record(stream)
+        lbv.lbv_moe_gemm_w13_silu(cfg, x, w13, sw13, off, srt, act, gws, stream)
+        evs_[3].record(stream)
         lbv.lbv_moe_gemm_w2_combine(cfg, act, w2, sw2, off, srt, inv, wts, out, yws, stream)
-        evs[4].record(stream)
+        evs_[4].record(stream)
 
-    nst = max(5, min(args.steps, 20))
+    nst = max(5, min(args.steps, 30))
     evsets = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(nst)]
     for _ in range(2):
         split(evsets[0])
@@ -141,10 +193,10 @@ def main():
     for i in range(nst):
         split(evsets[i])
     torch.cuda.synchronize()
-    stage_ms = {s: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evsets]))
-                for j, s in enumerate(stages)}
+    stage_runs = {s: [e[j].elapsed_time(e[j + 1]) for e in evsets] for j, s in enumerate(stages)}
+    stage_ms = {s: float(np.mean(v)) for s, v in stage_runs.items()}
 
-    # ---- algorithmic work ----------------------------------------------------------
+    # ---- algorithmic work -----------------------------------------------------------
     ids_h = ids.cpu().numpy()
     R_routed = int((ids_h >= 0).sum())
     Rp = R_routed + T * NS
@@ -155,9 +207,31 @@ def main():
     gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
     routed_tflops = 6.0 * H * I * R_routed / (gemm_ms * 1e-3) / 1e12
     valid_tokens = T if inp["mask"] is None else int(inp["mask"].sum())
-    w13_tflops = flops_w13 / (stage_ms["gemm_w13_silu"] * 1e-3) / 1e12
     counts = np.bincount(ids_h[ids_h >= 0].reshape(-1), minlength=E)
+    hit = counts > 0
+    # gate/up GEMM bytes per launch: the w13 rows of every expert hit, the
+    # shared gate/up rows, x read once, act written once
+    w13_bytes = (int(hit.sum()) * 2 * I * H + 2 * I * NS * H) * esz
+    bytes_w13 = w13_bytes + T * H * esz + Rp * I * esz
+    ai_w13 = flops_w13 / bytes_w13
+    w13_s = stage_ms["gemm_w13_silu"] * 1e-3
+    if ai_w13 < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        roof = {"bound": "hbm", "achieved": bytes_w13 / w13_s / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "algorithmic_bytes_per_launch": bytes_w13}
+    else:
+        roof = {"bound": "mfma", "achieved": flops_w13 / w13_s / 1e12, "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "algorithmic_flops_per_launch": flops_w13}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = recorded_traffic(wl.name, "gemm_w13_silu")
+    roof["kernel"] = "gemm_w13_silu (lbv_moe_gemm_w13_silu)"
+    roof["kernel_ms"] = stage_ms["gemm_w13_silu"]
+    roof["arithmetic_intensity_flop_per_byte"] = ai_w13
 
+    route_s = stage_ms["route"] * 1e-3
+    route_flops = 2.0 * H * E * T
+    perm_bytes = T * K * 4 + 2 * T * KS * 4 + (S + 1) * 4
+    weight_bytes = (int(hit.sum()) * 3 * I * H + 3 * I * NS * H) * esz
+    block_bytes = weight_bytes + 2 * T * H * esz + 8 * T * K + E * H * 4
     res = {
         "metric": "MoE-layer tokens/s",
         "value": T / (ms_per_step * 1e-3),
@@ -171,29 +245,33 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if bf else "f32",
         "data": "synthetic (seeded, shapes of the LingBot-Video video workloads)",
-        "config": {"workload": wl.name, "tokens": T, "hidden": H, "num_experts": E,
-                   "top_k": K, "n_group": wl.n_group, "topk_group": wl.topk_group,
-                   "intermediate": I, "n_shared": NS, "routed_rows": R_routed},
+        "config": {"workload": wl.name, "tokens": T, "valid_tokens": valid_tokens, "hidden": H,
+                   "num_experts": E, "top_k": K, "n_group": wl.n_group,
+                   "topk_group": wl.topk_group, "intermediate": I, "n_shared": NS,
+                   "routed_rows": R_routed},
+        "step_ms": {"median": pct(per_step, 50), "p10": pct(per_step, 10),
+                    "p90": pct(per_step, 90), "n": len(per_step)},
         "grouped_gemm_tflops": gemm_tflops,
         "grouped_gemm_frac_bf16_peak": gemm_tflops / BF16_PEAK_TFLOPS,
         "routed_gemm_tflops": routed_tflops,
         "valid_tokens_per_s": valid_tokens / (ms_per_step * 1e-3),
         "stage_ms": stage_ms,
-        "router_x_read_gbs": T * H * (2 if bf else 4) / (stage_ms["route"] * 1e-3) / 1e9,
+        "stage_ms_p90": {s: pct(v, 90) for s, v in stage_runs.items()},
+        "block_hbm_frac": block_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "router": {"x_read_gbs": T * H * esz / route_s / 1e9,
+                   "fp32_equiv_tflops": route_flops / route_s / 1e12,
+                   "frac_fp32_peak": route_flops / route_s / 1e12 / FP32_PEAK_TFLOPS},
+        "permute": {"bytes": perm_bytes, "gbs": perm_bytes / (stage_ms["permute"] * 1e-3) / 1e9,
+                    "frac_hbm": perm_bytes / (stage_ms["permute"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "expert_load_max_over_mean": float(counts.max() / max(counts.mean(), 1e-9)),
-        "roofline": {
-            "kernel": "gemm_w13_silu (lbv_moe_gemm_w13_silu)",
-            "bound": "mfma",
-            "achieved": w13_tflops,
-            "peak": BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": w13_tflops / BF16_PEAK_TFLOPS,
-            "traffic": GEMM_W13_TRAFFIC_BYTES,
-            "algorithmic_flops_per_launch": flops_w13,
-        },
+        "roofline": roof,
+        "kernel_source_sha256": kernel_source_hash(),
+        "input_sha256": digests,
         "wall_s_timed": wall,
         "input_gen_s": t_gen,
     }
+    if wl.hot:
+        res["hot_expert_share"] = float(counts[list(wl.hot)].sum() / max(counts.sum(), 1))
 
     # ---- CPU oracle on a bounded sample of the same workload -----------------------
     if not args.no_cpu_baseline:
@@ -208,7 +286,7 @@ def main():
                            inp["w2"], inp["shared_w13"], inp["shared_w2"], m)
         dt = time.perf_counter() - tc
         res["cpu_baseline"] = {"value": n / dt, "unit": "tokens/s", "cores": threads,
-                               "kind": "oracle",
+                               "kind": "oracle", "cpu_model": cpu_model(),
                                "sample": "%d of %d tokens of %s, evenly spaced; %.1f s" %
                                          (n, T, wl.name, dt)}
     print(json.dumps(res), flush=True)

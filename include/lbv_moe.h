@@ -93,7 +93,8 @@ typedef struct {
     int32_t dtype;                   /* lbv_dtype                           */
 } lbv_moe_config;
 
-/* Version of this ABI (bumped on any signature or layout change). */
+/* Version of this ABI (bumped on any signature or layout change; 2: the
+ * gate/up call takes a workspace). */
 int32_t lbv_abi_version(void);
 
 /* Human-readable name of a status code (static storage). */
@@ -107,10 +108,12 @@ lbv_status lbv_moe_check_config(const lbv_moe_config *cfg);
  *   lbv_moe_workspace_size:          for lbv_moe_forward;
  *   lbv_moe_route_workspace_size:    for lbv_moe_route (does not depend on T;
  *                                    on the bf16 path 3 E H bf16 values, rounded
- *                                    up to 256 bytes, plus 4 x 4096 x EP fp32
- *                                    partial logits for calls of at most 4096
- *                                    tokens, EP = 64 if E <= 64 else 128; else 0);
+ *                                    up to 256 bytes, plus 4096 x EP fp32
+ *                                    logits for calls of at most 4096 tokens,
+ *                                    EP = 64 if E <= 64 else 128; else 0);
  *   lbv_moe_permute_workspace_size:  for lbv_moe_permute;
+ *   lbv_moe_w13_workspace_size:      for lbv_moe_gemm_w13_silu (256 bytes of
+ *                                    tile queue counters);
  *   lbv_moe_w2_workspace_size:       for lbv_moe_gemm_w2_combine.
  * Sizes grow linearly with T (the forward one is dominated by the bf16 expert
  * output buffer, T (K + ns) H elements).
@@ -118,6 +121,7 @@ lbv_status lbv_moe_check_config(const lbv_moe_config *cfg);
 lbv_status lbv_moe_workspace_size(const lbv_moe_config *cfg, int64_t T, size_t *bytes);
 lbv_status lbv_moe_route_workspace_size(const lbv_moe_config *cfg, size_t *bytes);
 lbv_status lbv_moe_permute_workspace_size(const lbv_moe_config *cfg, int64_t T, size_t *bytes);
+lbv_status lbv_moe_w13_workspace_size(const lbv_moe_config *cfg, int64_t T, size_t *bytes);
 lbv_status lbv_moe_w2_workspace_size(const lbv_moe_config *cfg, int64_t T, size_t *bytes);
 
 /*
@@ -137,7 +141,9 @@ lbv_status lbv_moe_w2_workspace_size(const lbv_moe_config *cfg, int64_t T, size_
  *                     is exactly W_r, so the fp32 logits run on the bf16
  *                     matrix cores; finite W_r entries must stay below the
  *                     bf16 overflow threshold (about 3.39e38).  Calls of at
- *                     most 4096 tokens also keep partial logits there.
+ *                     most 4096 tokens also keep their logits there.  A
+ *                     token's ids and weights do not depend on the other
+ *                     tokens of the call, nor on how many there are.
  * Ties between equal scores go to the lower group / expert index.
  */
 lbv_status lbv_moe_route(const lbv_moe_config *cfg, int64_t T, const void *x,
@@ -179,12 +185,14 @@ lbv_status lbv_moe_permute(const lbv_moe_config *cfg, int64_t T, const int32_t *
  * once to cfg->dtype.
  *   x [T, H]; w13 [E, 2I, H]; shared_w13 [2 I_s, H] (NULL iff ns == 0);
  *   offsets, sorted_rows from lbv_moe_permute;
- *   act [T (K + ns), I] out (rows [0, R) written).
+ *   act [T (K + ns), I] out (rows [0, R) written);
+ *   ws, ws_bytes: lbv_moe_w13_workspace_size bytes of scratch (tile queue
+ *   counters, reset by the call itself on `stream`).
  */
 lbv_status lbv_moe_gemm_w13_silu(const lbv_moe_config *cfg, int64_t T, const void *x,
                                  const void *w13, const void *shared_w13,
                                  const int32_t *offsets, const int32_t *sorted_rows,
-                                 void *act, hipStream_t stream);
+                                 void *act, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Grouped down projection and weighted combine (PR #32341 summary, excerpt:

@@ -18,7 +18,7 @@ import torch  # noqa: F401  (loads the HIP runtime that the library binds to)
 __all__ = [
     "LbvError", "MoEConfig", "config", "load", "lbv_abi_version", "lbv_status_string",
     "lbv_moe_check_config", "lbv_moe_workspace_size", "lbv_moe_route_workspace_size",
-    "lbv_moe_permute_workspace_size",
+    "lbv_moe_permute_workspace_size", "lbv_moe_w13_workspace_size",
     "lbv_moe_w2_workspace_size", "lbv_moe_route", "lbv_moe_permute", "lbv_moe_gemm_w13_silu",
     "lbv_moe_gemm_w2_combine", "lbv_moe_forward", "EXPORTS", "LIB_PATH",
 ]
@@ -33,7 +33,8 @@ LBV_SCORE_SIGMOID, LBV_SCORE_SOFTMAX = 0, 1
 
 EXPORTS = (
     "lbv_abi_version", "lbv_status_string", "lbv_moe_check_config", "lbv_moe_workspace_size",
-    "lbv_moe_route_workspace_size", "lbv_moe_permute_workspace_size", "lbv_moe_w2_workspace_size", "lbv_moe_route",
+    "lbv_moe_route_workspace_size", "lbv_moe_permute_workspace_size", "lbv_moe_w13_workspace_size",
+    "lbv_moe_w2_workspace_size", "lbv_moe_route",
     "lbv_moe_permute", "lbv_moe_gemm_w13_silu", "lbv_moe_gemm_w2_combine", "lbv_moe_forward",
 )
 
@@ -95,7 +96,7 @@ def load():
     L.lbv_status_string.argtypes, L.lbv_status_string.restype = [st], ctypes.c_char_p
     L.lbv_moe_check_config.argtypes, L.lbv_moe_check_config.restype = [C], st
     for n in ("lbv_moe_workspace_size", "lbv_moe_permute_workspace_size",
-              "lbv_moe_w2_workspace_size"):
+              "lbv_moe_w13_workspace_size", "lbv_moe_w2_workspace_size"):
         getattr(L, n).argtypes = [C, I64, ctypes.POINTER(SZ)]
         getattr(L, n).restype = st
     L.lbv_moe_route_workspace_size.argtypes = [C, ctypes.POINTER(SZ)]
@@ -104,7 +105,7 @@ def load():
     L.lbv_moe_route.restype = st
     L.lbv_moe_permute.argtypes = [C, I64, P, P, P, P, P, SZ, P]
     L.lbv_moe_permute.restype = st
-    L.lbv_moe_gemm_w13_silu.argtypes = [C, I64, P, P, P, P, P, P, P]
+    L.lbv_moe_gemm_w13_silu.argtypes = [C, I64, P, P, P, P, P, P, P, SZ, P]
     L.lbv_moe_gemm_w13_silu.restype = st
     L.lbv_moe_gemm_w2_combine.argtypes = [C, I64, P, P, P, P, P, P, P, P, P, SZ, P]
     L.lbv_moe_gemm_w2_combine.restype = st
@@ -130,6 +131,49 @@ def _ptr(t: Optional[torch.Tensor], name: str, dtype=None):
     if dtype is not None and t.dtype != dtype:
         raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
     return t.data_ptr()
+
+
+def _dims(cfg: MoEConfig):
+    H, E, K, I, ns = (cfg.hidden, cfg.num_experts, cfg.top_k, cfg.intermediate,
+                      cfg.n_shared_experts)
+    return H, E, K, I, ns, K + ns, E + ns
+
+
+def _shape(t, name, *shape):
+    """Checks t.shape against `shape` (None entries are free); None tensors pass."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor or None" % name)
+    got = tuple(t.shape)
+    if len(got) != len(shape) or any(w is not None and g != w for g, w in zip(got, shape)):
+        raise ValueError("%s has shape %s, expected %s" % (
+            name, list(got), ["*" if w is None else w for w in shape]))
+
+
+def _numel_at_least(t, name, n):
+    if t is not None and t.numel() < n:
+        raise ValueError("%s holds %d elements, needs at least %d" % (name, t.numel(), n))
+
+
+def _need(t, name):
+    if t is None:
+        raise ValueError("%s is required" % name)
+
+
+def _same_device(*ts):
+    devs = {t.device for t in ts if isinstance(t, torch.Tensor)}
+    if len(devs) > 1:
+        raise ValueError("all tensors must be on one device, got %s" % sorted(map(str, devs)))
+
+
+def _shared_shapes(cfg, shared_w13, shared_w2):
+    H, E, K, I, ns, KS, S = _dims(cfg)
+    if ns > 0:
+        _shape(shared_w13, "shared_w13", 2 * I * ns, H)
+        _shape(shared_w2, "shared_w2", H, I * ns)
+    elif shared_w13 is not None or shared_w2 is not None:
+        raise ValueError("shared weights given but n_shared_experts == 0")
 
 
 def _stream(stream):
@@ -178,14 +222,27 @@ def lbv_moe_permute_workspace_size(cfg: MoEConfig, T: int) -> int:
     return _size("lbv_moe_permute_workspace_size", cfg, T)
 
 
+def lbv_moe_w13_workspace_size(cfg: MoEConfig, T: int) -> int:
+    return _size("lbv_moe_w13_workspace_size", cfg, T)
+
+
 def lbv_moe_w2_workspace_size(cfg: MoEConfig, T: int) -> int:
     return _size("lbv_moe_w2_workspace_size", cfg, T)
 
 
 def lbv_moe_route(cfg, x, router_w, e_bias, mask, topk_ids, topk_w, ws=None, stream=None):
     dt = cfg.torch_dtype
+    H, E, K, I, ns, KS, S = _dims(cfg)
+    _shape(x, "x", None, H)
+    T = x.shape[0]
+    _shape(router_w, "router_w", E, H)
+    _shape(e_bias, "e_bias", E)
+    _shape(mask, "mask", T)
+    _shape(topk_ids, "topk_ids", T, K)
+    _shape(topk_w, "topk_w", T, K)
+    _same_device(x, router_w, e_bias, mask, topk_ids, topk_w, ws)
     _check(load().lbv_moe_route(
-        ctypes.byref(cfg), x.shape[0], _ptr(x, "x", dt), _ptr(router_w, "router_w", torch.float32),
+        ctypes.byref(cfg), T, _ptr(x, "x", dt), _ptr(router_w, "router_w", torch.float32),
         _ptr(e_bias, "e_bias", torch.float32), _ptr(mask, "mask", torch.uint8),
         _ptr(topk_ids, "topk_ids", torch.int32), _ptr(topk_w, "topk_w", torch.float32),
         _ptr(ws, "ws"), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
@@ -193,27 +250,59 @@ def lbv_moe_route(cfg, x, router_w, e_bias, mask, topk_ids, topk_w, ws=None, str
 
 
 def lbv_moe_permute(cfg, topk_ids, offsets, sorted_rows, inv_rows, ws, stream=None):
+    H, E, K, I, ns, KS, S = _dims(cfg)
+    _shape(topk_ids, "topk_ids", None, K)
+    T = topk_ids.shape[0]
+    _numel_at_least(offsets, "offsets", S + 1)
+    _numel_at_least(sorted_rows, "sorted_rows", T * KS)
+    _numel_at_least(inv_rows, "inv_rows", T * KS)
+    _need(ws, "ws")
+    _same_device(topk_ids, offsets, sorted_rows, inv_rows, ws)
     _check(load().lbv_moe_permute(
-        ctypes.byref(cfg), topk_ids.shape[0], _ptr(topk_ids, "topk_ids", torch.int32),
+        ctypes.byref(cfg), T, _ptr(topk_ids, "topk_ids", torch.int32),
         _ptr(offsets, "offsets", torch.int32), _ptr(sorted_rows, "sorted_rows", torch.int32),
         _ptr(inv_rows, "inv_rows", torch.int32), _ptr(ws, "ws"),
         ws.numel() * ws.element_size(), _stream(stream)), "lbv_moe_permute")
 
 
-def lbv_moe_gemm_w13_silu(cfg, x, w13, shared_w13, offsets, sorted_rows, act, stream=None):
+def lbv_moe_gemm_w13_silu(cfg, x, w13, shared_w13, offsets, sorted_rows, act, ws, stream=None):
     dt = cfg.torch_dtype
+    H, E, K, I, ns, KS, S = _dims(cfg)
+    _shape(x, "x", None, H)
+    T = x.shape[0]
+    _shape(w13, "w13", E, 2 * I, H)
+    _shared_shapes(cfg, shared_w13, None)
+    _numel_at_least(offsets, "offsets", S + 1)
+    _numel_at_least(sorted_rows, "sorted_rows", T * KS)
+    _shape(act, "act", None, I)
+    _numel_at_least(act, "act", T * KS * I)
+    _need(ws, "ws")
+    _same_device(x, w13, shared_w13, offsets, sorted_rows, act, ws)
     _check(load().lbv_moe_gemm_w13_silu(
-        ctypes.byref(cfg), x.shape[0], _ptr(x, "x", dt), _ptr(w13, "w13", dt),
+        ctypes.byref(cfg), T, _ptr(x, "x", dt), _ptr(w13, "w13", dt),
         _ptr(shared_w13, "shared_w13", dt), _ptr(offsets, "offsets", torch.int32),
-        _ptr(sorted_rows, "sorted_rows", torch.int32), _ptr(act, "act", dt), _stream(stream)),
-        "lbv_moe_gemm_w13_silu")
+        _ptr(sorted_rows, "sorted_rows", torch.int32), _ptr(act, "act", dt), _ptr(ws, "ws"),
+        ws.numel() * ws.element_size(), _stream(stream)), "lbv_moe_gemm_w13_silu")
 
 
 def lbv_moe_gemm_w2_combine(cfg, act, w2, shared_w2, offsets, sorted_rows, inv_rows, topk_w,
                             out, ws, stream=None):
     dt = cfg.torch_dtype
+    H, E, K, I, ns, KS, S = _dims(cfg)
+    _shape(out, "out", None, H)
+    T = out.shape[0]
+    _shape(act, "act", None, I)
+    _numel_at_least(act, "act", T * KS * I)
+    _shape(w2, "w2", E, H, I)
+    _shared_shapes(cfg, None, shared_w2)
+    _numel_at_least(offsets, "offsets", S + 1)
+    _numel_at_least(sorted_rows, "sorted_rows", T * KS)
+    _numel_at_least(inv_rows, "inv_rows", T * KS)
+    _shape(topk_w, "topk_w", T, K)
+    _need(ws, "ws")
+    _same_device(act, w2, shared_w2, offsets, sorted_rows, inv_rows, topk_w, out, ws)
     _check(load().lbv_moe_gemm_w2_combine(
-        ctypes.byref(cfg), out.shape[0], _ptr(act, "act", dt), _ptr(w2, "w2", dt),
+        ctypes.byref(cfg), T, _ptr(act, "act", dt), _ptr(w2, "w2", dt),
         _ptr(shared_w2, "shared_w2", dt), _ptr(offsets, "offsets", torch.int32),
         _ptr(sorted_rows, "sorted_rows", torch.int32), _ptr(inv_rows, "inv_rows", torch.int32),
         _ptr(topk_w, "topk_w", torch.float32), _ptr(out, "out", dt), _ptr(ws, "ws"),
@@ -223,8 +312,23 @@ def lbv_moe_gemm_w2_combine(cfg, act, w2, shared_w2, offsets, sorted_rows, inv_r
 def lbv_moe_forward(cfg, x, mask, router_w, e_bias, w13, w2, shared_w13, shared_w2, out,
                     topk_ids_out, topk_w_out, ws, stream=None):
     dt = cfg.torch_dtype
+    H, E, K, I, ns, KS, S = _dims(cfg)
+    _shape(x, "x", None, H)
+    T = x.shape[0]
+    _shape(mask, "mask", T)
+    _shape(router_w, "router_w", E, H)
+    _shape(e_bias, "e_bias", E)
+    _shape(w13, "w13", E, 2 * I, H)
+    _shape(w2, "w2", E, H, I)
+    _shared_shapes(cfg, shared_w13, shared_w2)
+    _shape(out, "out", T, H)
+    _shape(topk_ids_out, "topk_ids_out", T, K)
+    _shape(topk_w_out, "topk_w_out", T, K)
+    _need(ws, "ws")
+    _same_device(x, mask, router_w, e_bias, w13, w2, shared_w13, shared_w2, out, topk_ids_out,
+                 topk_w_out, ws)
     _check(load().lbv_moe_forward(
-        ctypes.byref(cfg), x.shape[0], _ptr(x, "x", dt), _ptr(mask, "mask", torch.uint8),
+        ctypes.byref(cfg), T, _ptr(x, "x", dt), _ptr(mask, "mask", torch.uint8),
         _ptr(router_w, "router_w", torch.float32), _ptr(e_bias, "e_bias", torch.float32),
         _ptr(w13, "w13", dt), _ptr(w2, "w2", dt), _ptr(shared_w13, "shared_w13", dt),
         _ptr(shared_w2, "shared_w2", dt), _ptr(out, "out", dt),

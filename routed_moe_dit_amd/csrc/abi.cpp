@@ -13,7 +13,7 @@ using lbv::Dims;
 
 namespace {
 
-constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kAbiVersion = 2;
 constexpr size_t kAlign = 256;
 
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -63,7 +63,11 @@ lbv_status make_dims(const lbv_moe_config* c, int64_t T, Dims* d) {
     // row indices and offsets are int32
     if (T > 0 && T > (int64_t)INT32_MAX / KS) return LBV_ERR_SHAPE;
     // the bf16 gate/up matmul gathers rows of x with 32-bit byte offsets
-    if (c->dtype == LBV_BF16 && (T * c->hidden * 2 >= (1ll << 32) || T >= (1 << 24))) return LBV_ERR_SHAPE;
+    // and the down matmul addresses act rows of a segment (at most T of them)
+    // with 32-bit byte offsets
+    if (c->dtype == LBV_BF16 && (T * c->hidden * 2 >= (1ll << 32) || T >= (1 << 24) ||
+                                 T * c->intermediate * 2 >= (1ll << 32)))
+        return LBV_ERR_SHAPE;
     d->T = T;
     d->H = c->hidden;
     d->E = c->num_experts;
@@ -89,7 +93,7 @@ size_t elem_bytes(const Dims& d) { return d.bf16 ? 2 : 4; }
 
 // Forward workspace layout (each part 256-byte aligned).
 struct FwdLayout {
-    size_t ids, w, offsets, sorted, inv, perm, route, act, y, total;
+    size_t ids, w, offsets, sorted, inv, perm, route, ctr1, ctr2, act, y, total;
 };
 
 FwdLayout fwd_layout(const Dims& d) {
@@ -103,15 +107,21 @@ FwdLayout fwd_layout(const Dims& d) {
     L.inv = off;     off += round_up(T * d.KS * sizeof(int32_t));
     L.perm = off;    off += round_up(lbv::permute_ws_bytes(d));
     L.route = off;   off += round_up(lbv::route_ws_bytes(d));
+    L.ctr1 = off;    off += round_up(lbv::kGemmCtrBytes);
+    L.ctr2 = off;    off += round_up(lbv::kGemmCtrBytes);
     L.act = off;     off += round_up(T * d.KS * d.I * elem_bytes(d));
     L.y = off;       off += round_up(T * d.KS * d.H * elem_bytes(d));
     L.total = off;
     return L;
 }
 
-size_t w2_ws_bytes(const Dims& d) {
+// down matmul workspace: the expert outputs y [T (K + ns), H], then the tile
+// queue counters
+size_t w2_y_bytes(const Dims& d) {
     return round_up(static_cast<size_t>(d.T) * d.KS * d.H * elem_bytes(d));
 }
+size_t w2_ws_bytes(const Dims& d) { return w2_y_bytes(d) + round_up(lbv::kGemmCtrBytes); }
+size_t w13_ws_bytes(const Dims&) { return round_up(lbv::kGemmCtrBytes); }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
@@ -169,6 +179,15 @@ lbv_status lbv_moe_permute_workspace_size(const lbv_moe_config* cfg, int64_t T, 
     return LBV_OK;
 }
 
+lbv_status lbv_moe_w13_workspace_size(const lbv_moe_config* cfg, int64_t T, size_t* bytes) {
+    if (!bytes) return LBV_ERR_NULL;
+    Dims d;
+    lbv_status st = make_dims(cfg, T, &d);
+    if (st != LBV_OK) return st;
+    *bytes = w13_ws_bytes(d);
+    return LBV_OK;
+}
+
 lbv_status lbv_moe_w2_workspace_size(const lbv_moe_config* cfg, int64_t T, size_t* bytes) {
     if (!bytes) return LBV_ERR_NULL;
     Dims d;
@@ -214,17 +233,19 @@ lbv_status lbv_moe_permute(const lbv_moe_config* cfg, int64_t T, const int32_t* 
 lbv_status lbv_moe_gemm_w13_silu(const lbv_moe_config* cfg, int64_t T, const void* x,
                                  const void* w13, const void* shared_w13,
                                  const int32_t* offsets, const int32_t* sorted_rows,
-                                 void* act, hipStream_t stream) {
+                                 void* act, void* ws, size_t ws_bytes, hipStream_t stream) {
     Dims d;
     lbv_status st = make_dims(cfg, T, &d);
     if (st != LBV_OK) return st;
     if (T == 0) return LBV_OK;
-    if (!x || !w13 || !offsets || !sorted_rows || !act) return LBV_ERR_NULL;
+    if (!x || !w13 || !offsets || !sorted_rows || !act || !ws) return LBV_ERR_NULL;
     if (d.NS > 0 && !shared_w13) return LBV_ERR_NULL;
     if (!aligned16(x) || !aligned16(w13) || !aligned16(shared_w13) || !aligned16(act) ||
-        !aligned4(offsets) || !aligned4(sorted_rows))
+        !aligned4(offsets) || !aligned4(sorted_rows) || !aligned16(ws))
         return LBV_ERR_ALIGN;
-    return hip_status(lbv::launch_gemm_w13(d, x, w13, shared_w13, offsets, sorted_rows, act, stream));
+    if (ws_bytes < w13_ws_bytes(d)) return LBV_ERR_WORKSPACE;
+    return hip_status(lbv::launch_gemm_w13(d, x, w13, shared_w13, offsets, sorted_rows, act,
+                                           static_cast<int*>(ws), stream));
 }
 
 lbv_status lbv_moe_gemm_w2_combine(const lbv_moe_config* cfg, int64_t T, const void* act,
@@ -244,7 +265,8 @@ lbv_status lbv_moe_gemm_w2_combine(const lbv_moe_config* cfg, int64_t T, const v
         !aligned4(topk_w))
         return LBV_ERR_ALIGN;
     if (ws_bytes < w2_ws_bytes(d)) return LBV_ERR_WORKSPACE;
-    hipError_t e = lbv::launch_gemm_w2(d, act, w2, shared_w2, offsets, sorted_rows, ws, stream);
+    int* ctr = reinterpret_cast<int*>(static_cast<char*>(ws) + w2_y_bytes(d));
+    hipError_t e = lbv::launch_gemm_w2(d, act, w2, shared_w2, offsets, sorted_rows, ws, ctr, stream);
     if (e != hipSuccess) return LBV_ERR_HIP;
     return hip_status(lbv::launch_combine(d, ws, inv_rows, topk_w, out, stream));
 }
@@ -279,11 +301,13 @@ lbv_status lbv_moe_forward(const lbv_moe_config* cfg, int64_t T, const void* x,
     void* rws = base + L.route;
     void* act = base + L.act;
     void* y = base + L.y;
+    int* ctr1 = reinterpret_cast<int*>(base + L.ctr1);
+    int* ctr2 = reinterpret_cast<int*>(base + L.ctr2);
 
     hipError_t e = lbv::launch_route(d, x, router_w, e_bias, mask, ids, w, rws, stream);
     if (e == hipSuccess) e = lbv::launch_permute(d, ids, offsets, sorted, inv, perm, stream);
-    if (e == hipSuccess) e = lbv::launch_gemm_w13(d, x, w13, shared_w13, offsets, sorted, act, stream);
-    if (e == hipSuccess) e = lbv::launch_gemm_w2(d, act, w2, shared_w2, offsets, sorted, y, stream);
+    if (e == hipSuccess) e = lbv::launch_gemm_w13(d, x, w13, shared_w13, offsets, sorted, act, ctr1, stream);
+    if (e == hipSuccess) e = lbv::launch_gemm_w2(d, act, w2, shared_w2, offsets, sorted, y, ctr2, stream);
     if (e == hipSuccess) e = lbv::launch_combine(d, y, inv, w, out, stream);
     return hip_status(e);
 }

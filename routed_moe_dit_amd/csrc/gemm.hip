@@ -87,7 +87,7 @@
 #define LBV_G2_ORDER 1024
 #endif
 #ifndef LBV_FEW_ROWS
-#define LBV_FEW_ROWS 96
+#define LBV_FEW_ROWS 256
 #endif
 #ifndef LBV_FEW_STAGES
 #define LBV_FEW_STAGES 3
@@ -124,6 +124,7 @@ struct GemmArgs {
     int kdim;               // reduction length: H (gate/up) or I (down)
     int ncols;              // output columns: I (gate/up) or H (down)
     int ntn;                // n-tiles per m-tile
+    int* ctr;               // [8] tile queue counters, zero at launch (one per XCD)
 };
 
 // Finds the segment and first row of logical m-tile `mt` for tiles of BM rows
@@ -226,6 +227,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     __shared__ int s_pre[kMaxSeg + 1];           // m-tiles before segment s
     __shared__ int s_rid[BM];                    // slot ids of a tile's rows: gate/up: the next tile's; down: this tile's
     __shared__ int s_tmp[8];
+    __shared__ int s_claim[2];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -269,15 +271,61 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         __syncthreads();
     }
     const int NT = __builtin_amdgcn_readfirstlane(s_pre[a.S]) * a.ntn;
-    const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8, nslot = gridDim.x / 8;
-    const int c1 = static_cast<int>(static_cast<int64_t>(NT) * (xcd + 1) / 8);
-    int t = static_cast<int>(static_cast<int64_t>(NT) * xcd / 8) + slot;
-    if (t >= c1) return;
+    const int xcd = blockIdx.x % 8;
+    constexpr int WOUT = MODE == 0 ? BN / 2 : BN;          // output columns of a tile
+    const int ncols_all = MODE == 0 ? a.I : a.H;
+    // ---- tile queues: XCD q owns the logical tiles NT q / 8 .. NT (q+1) / 8 - 1
+    // (a contiguous range, so that the tiles in flight on one XCD share
+    // operand rows in its L2) and hands them out in order through counter
+    // a.ctr[q].  A workgroup takes tiles from its own XCD's queue, then,
+    // once that is empty, from the other XCDs' queues in turn, so that the
+    // XCDs finish together although tile costs differ (e.g. the shared
+    // expert's contiguous rows run faster).  Which workgroup computes a tile
+    // does not change its result.  Thread 0 claims; claims reach the other
+    // threads through s_claim, one tile ahead: claim i + 2 is issued at the
+    // start of tile i and resolved after its k-loop (so that the atomic's
+    // round trip overlaps the MFMAs), into the slot tile i's claim came from.
+    int qk = 0;                                            // queues found empty (thread 0)
+    auto qrange = [&](int q, int& q0, int& q1) {
+        q0 = static_cast<int>(static_cast<int64_t>(NT) * q / 8);
+        q1 = static_cast<int>(static_cast<int64_t>(NT) * (q + 1) / 8);
+    };
+    auto claim = [&]() -> int {
+        while (qk < 8) {
+            const int q = (xcd + qk) & 7;
+            int q0, q1;
+            qrange(q, q0, q1);
+            const int u = atomicAdd(&a.ctr[q], 1);
+            if (u < q1 - q0) return q0 + u;
+            ++qk;
+        }
+        return -1;
+    };
+    int pend_u = 0;                                        // thread 0: issued claim of queue
+    auto claim_issue = [&]() {                             // (xcd + qk) & 7
+        if (qk < 8) pend_u = atomicAdd(&a.ctr[(xcd + qk) & 7], 1);
+    };
+    auto claim_resolve = [&]() -> int {
+        if (qk >= 8) return -1;
+        int q0, q1;
+        qrange((xcd + qk) & 7, q0, q1);
+        if (pend_u < q1 - q0) return q0 + pend_u;
+        ++qk;
+        return claim();
+    };
+    if (tid == 0) {
+        s_claim[0] = claim();
+        s_claim[1] = claim();
+    }
+    __syncthreads();
+    int t = __builtin_amdgcn_readfirstlane(s_claim[0]);
+    if (t < 0) return;
+    int it = 0;                                            // tiles done by this workgroup
 
     // ---- tile lookup: a forward walk over the segment table from the last
     // tile's segment (restarted from 0 if a tile index goes backwards) ----------
     int walk = 0;
-    auto locate = [&](int tt, int& seg_, int& m0_, int& nt_) {
+    auto locate = [&](int tt, int& seg_, int& m0_, int& nt_, int& lo_, int& hi_) {
         // Inside a segment the m-tiles form blocks of ORDER (the last one
         // shorter); a block's tiles run n-tile major, so that the tiles that
         // share one weight slice are adjacent and those that share token rows
@@ -293,6 +341,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         const int pb = nm - blk * ORDER < ORDER ? nm - blk * ORDER : ORDER;   // m-tiles in this block
         nt_ = r / pb;
         m0_ = (blk * ORDER + (r - nt_ * pb)) * BM;
+        // output columns lo_ .. hi_ (the last n-tile may be partial)
+        lo_ = nt_ * WOUT;
+        hi_ = lo_ + WOUT - 1 < ncols_all - 1 ? lo_ + WOUT - 1 : ncols_all - 1;
     };
 
     // ---- copy sources: a wave-uniform base (scalar registers, advanced by BK
@@ -316,7 +367,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     };
     // Points the copy sources at tile (seg_, m0_, nt_); gate/up reads the slot
     // ids from s_rid, which must have landed (and be visible: a barrier).
-    auto set_sources = [&](int seg_, int seg_r0_, int seg_n_, int m0_, int nt_) {
+    auto set_sources = [&](int seg_, int seg_r0_, int seg_n_, int m0_, int nt_, int lo_, int hi_) {
         if (CW < NW && wave >= CW) return;       // not a copying wave
         // lane-derived terms are recomputed here rather than hoisted out of
         // the tile loop (where they would hold registers through the k-loop)
@@ -353,12 +404,18 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
             if (MODE == 0) {
                 const int half = r / (BN / 2);
                 int n = nt_ * (BN / 2) + (r % (BN / 2));
+                // rows past the last column (a partial last n-tile) repeat
+                // the last row: no extra HBM bytes
+                n = n < lo_ ? lo_ : n;
+                n = n > hi_ ? hi_ : n;
                 if (n >= a.I) n = a.I - 1;
                 const int row = shared_seg ? (half ? Is + jsh * a.I + n : jsh * a.I + n)
                                            : (half ? a.I + n : n);
                 boff[i] = (__umul24(row, a.H) + c * 8) * 2;
             } else {
                 int n = nt_ * BN + r;
+                n = n < lo_ ? lo_ : n;
+                n = n > hi_ ? hi_ : n;
                 if (n >= a.H) n = a.H - 1;
                 boff[i] = (__umul24(n, shared_seg ? Is : a.I) + c * 8) * 2;
             }
@@ -439,8 +496,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     using S2 = std::integral_constant<int, 2>;
 
     // ---- first tile: sources, k-tile 0 into stage 0, first slice read ----------
-    int seg, m0, nt;
-    locate(t, seg, m0, nt);
+    int seg, m0, nt, lo, hi;
+    locate(t, seg, m0, nt, lo, hi);
     int seg_r0 = a.offsets[seg];
     int seg_n = a.offsets[seg + 1] - seg_r0;
     if (MODE == 0) {
@@ -448,7 +505,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         wait_vmcnt<0>();
         block_barrier();
     }
-    set_sources(seg, seg_r0, seg_n, m0, nt);
+    set_sources(seg, seg_r0, seg_n, m0, nt, lo, hi);
     // k-tiles 0 .. STG-2 into stages 0 .. STG-2 (zero-filled past nk)
     auto pro_fill = [&](auto S, int kt) {
         if (kt < nk) {
@@ -512,7 +569,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     // current tile, its slot ids are copied at step 0, its copy sources are set
     // right after the barrier of the second-to-last step.
     bool has_next = false;
-    int nseg = 0, nm0 = 0, nnt = 0, nseg_r0 = 0, nseg_n = 0;
+    int nseg = 0, nm0 = 0, nnt = 0, nseg_r0 = 0, nseg_n = 0, nlo = 0, nhi = 0;
 
     // One k-tile kt held in stage S = kt % STG.  On entry slice 0 of it is in
     // set 0, and k-tiles kt+1 .. kt+STG-2 are in flight.  Slices 0 .. DSL-1
@@ -562,7 +619,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         wait_lgkmcnt0();
         block_barrier();
         if (kt == nkp - STG && has_next) {
-            set_sources(nseg, nseg_r0, nseg_n, nm0, nnt);
+            set_sources(nseg, nseg_r0, nseg_n, nm0, nnt, nlo, nhi);
             wait_lgkmcnt0();
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -590,10 +647,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     const int ncols = MODE == 0 ? a.I : a.H;
 
     for (;;) {
-        const int tn = t + nslot;
-        has_next = tn < c1;
+        const int tn = __builtin_amdgcn_readfirstlane(s_claim[(it + 1) & 1]);
+        has_next = tn >= 0;
+        if (tid == 0 && has_next) claim_issue();
         if (has_next) {
-            locate(tn, nseg, nm0, nnt);
+            locate(tn, nseg, nm0, nnt, nlo, nhi);
             nseg_r0 = a.offsets[nseg];
             nseg_n = a.offsets[nseg + 1] - nseg_r0;
         }
@@ -607,6 +665,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
             if constexpr (STG == 3) step(S2{}, kt + 2, std::false_type{});
         }
 
+        // the claim issued at this tile's start (read at the start of the next
+        // tile, after the barrier that follows the epilogue)
+        if (tid == 0 && has_next) s_claim[it & 1] = claim_resolve();
         // ---- epilogue: lane holds, for token tile i and weight tile j, output
         // columns 8q + 4*khalf + [0, 4) of token row (lane & 31).  Each wave
         // writes PROWS rows of its tile as bf16 into its staging region (row
@@ -662,7 +723,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
                 const u32x4 v = *reinterpret_cast<const u32x4*>(ep + ep_off(row, ch * 8));
                 // gate/up: act rows in segment order; down: y rows in slot order
                 const int64_t orow = MODE == 0 ? seg_r0 + m : s_rid[wm * (BM / 2) + p * PROWS + row];
-                if (m < seg_n && col < ncols) {
+                if (m < seg_n && col >= lo && col <= hi) {
                     u32x4* dst = reinterpret_cast<u32x4*>(C + orow * ncols + col);
                     if (MODE == 0 ? LBV_G1_EPI_NT : LBV_G2_EPI_NT) __builtin_nontemporal_store(v, dst);
                     else *dst = v;
@@ -677,16 +738,19 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         // the next tile's copy sources again (they were set for its k-tile 0
         // copies before the epilogue; re-forming them here keeps them out of
         // the epilogue's registers), and the fragment offsets
-        set_sources(nseg, nseg_r0, nseg_n, nm0, nnt);
+        set_sources(nseg, nseg_r0, nseg_n, nm0, nnt, nlo, nhi);
         frag_offsets();
 #pragma unroll
         for (int i = 0; i < TM; ++i) tf0[i] = *reinterpret_cast<const bf16x8*>(fa[0] + i * 32 * BK);
 #pragma unroll
         for (int j = 0; j < TN; ++j) wf0[j] = *reinterpret_cast<const bf16x8*>(fb[0] + brow(j) * BK);
         t = tn;
+        ++it;
         seg = nseg;
         m0 = nm0;
         nt = nnt;
+        lo = nlo;
+        hi = nhi;
         seg_r0 = nseg_r0;
         seg_n = nseg_n;
     }
@@ -887,6 +951,7 @@ GemmArgs make_args(const Dims& d) {
     a.NS = d.NS;
     a.KS = d.KS;
     a.S = d.S;
+    a.ctr = nullptr;
     return a;
 }
 
@@ -898,6 +963,12 @@ bool few_rows(const Dims& d) {
     return d.T * d.KS < static_cast<int64_t>(LBV_FEW_ROWS) * d.S;
 }
 
+// Zeroes the tile queue counters ahead of a grouped matmul on the same stream
+// (a kernel rather than a memset, so that the call can be captured in a graph).
+__global__ __launch_bounds__(64) void zero_ctr_kernel(int* ctr) {
+    if (threadIdx.x < 8) ctr[threadIdx.x] = 0;
+}
+
 int64_t max_mtiles(const Dims& d, int BM) {
     return (d.T * d.KS + BM - 1) / BM + d.S;
 }
@@ -906,8 +977,9 @@ int64_t max_mtiles(const Dims& d, int BM) {
 
 hipError_t launch_gemm_w13(const Dims& d, const void* x, const void* w13,
                            const void* shared_w13, const int32_t* offsets,
-                           const int32_t* sorted_rows, void* act, hipStream_t stream) {
+                           const int32_t* sorted_rows, void* act, int* ctr, hipStream_t stream) {
     GemmArgs a = make_args(d);
+    a.ctr = ctr;
     a.A = x;
     a.B = w13;
     a.Bsh = shared_w13;
@@ -918,6 +990,7 @@ hipError_t launch_gemm_w13(const Dims& d, const void* x, const void* w13,
     a.ncols = d.I;
     if (d.bf16) {
         a.ntn = (d.I + G1_BN / 2 - 1) / (G1_BN / 2);
+        hipLaunchKernelGGL(zero_ctr_kernel, dim3(1), dim3(64), 0, stream, ctr);
         if (few_rows(d))
             hipLaunchKernelGGL((gemm_bf16_kernel<64, G1_BN, 0, LBV_G1_WAVES, LBV_G1_COPY_WAVES, LBV_G1_ORDER, LBV_FEW_STAGES>),
                                dim3(cu_count() / 8 * 8), dim3(LBV_G1_WAVES * 64), 0, stream, a);
@@ -934,9 +1007,10 @@ hipError_t launch_gemm_w13(const Dims& d, const void* x, const void* w13,
 }
 
 hipError_t launch_gemm_w2(const Dims& d, const void* act, const void* w2, const void* shared_w2,
-                          const int32_t* offsets, const int32_t* sorted_rows, void* y,
+                          const int32_t* offsets, const int32_t* sorted_rows, void* y, int* ctr,
                           hipStream_t stream) {
     GemmArgs a = make_args(d);
+    a.ctr = ctr;
     a.A = act;
     a.B = w2;
     a.Bsh = shared_w2;
@@ -947,6 +1021,7 @@ hipError_t launch_gemm_w2(const Dims& d, const void* act, const void* w2, const 
     a.ncols = d.H;
     if (d.bf16) {
         a.ntn = (d.H + G2_BN - 1) / G2_BN;
+        hipLaunchKernelGGL(zero_ctr_kernel, dim3(1), dim3(64), 0, stream, ctr);
         if (few_rows(d))
             hipLaunchKernelGGL((gemm_bf16_kernel<64, G2_BN, 1, LBV_G2_WAVES, LBV_G2_COPY_WAVES, LBV_G2_ORDER, LBV_FEW_STAGES>),
                                dim3(cu_count() / 8 * 8), dim3(LBV_G2_WAVES * 64), 0, stream, a);

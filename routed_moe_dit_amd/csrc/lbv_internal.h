@@ -58,12 +58,16 @@ hipError_t launch_permute(const Dims& d, const int32_t* topk_ids, int32_t* offse
                           int32_t* sorted_rows, int32_t* inv_rows, void* ws,
                           hipStream_t stream);
 
+// The grouped matmuls take `ctr`: 8 ints of device scratch for their tile
+// queues (zeroed on the stream by the launcher).
+constexpr size_t kGemmCtrBytes = 256;
+
 hipError_t launch_gemm_w13(const Dims& d, const void* x, const void* w13,
                            const void* shared_w13, const int32_t* offsets,
-                           const int32_t* sorted_rows, void* act, hipStream_t stream);
+                           const int32_t* sorted_rows, void* act, int* ctr, hipStream_t stream);
 
 hipError_t launch_gemm_w2(const Dims& d, const void* act, const void* w2, const void* shared_w2,
-                          const int32_t* offsets, const int32_t* sorted_rows, void* y,
+                          const int32_t* offsets, const int32_t* sorted_rows, void* y, int* ctr,
                           hipStream_t stream);
 
 hipError_t launch_combine(const Dims& d, const void* y, const int32_t* inv_rows,

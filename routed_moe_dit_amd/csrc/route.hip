@@ -14,9 +14,10 @@
 //    route_bf16_kernel computes the fp32 logits on the bf16 matrix cores from
 //    an exact three-plane split of W_r, then routes two lanes per token (see
 //    the comment above it).
-//  * bf16 x, E <= 128, at most 4096 tokens: route_logits_kernel splits the
-//    same product along the hidden dimension over more workgroups and
-//    route_select_kernel adds the parts and routes one token per wave.
+//  * bf16 x, E <= 128, at most 4096 tokens: route_logits_kernel forms the
+//    same logits, in the same summation order, over many small workgroups,
+//    and route_select_kernel routes one token per wave; a token's routing is
+//    therefore the same on both sides of the switch.
 //  * otherwise (fp32 x, more experts or groups): route_kernel, one workgroup
 //    (4 waves) per 64 tokens, logits with v_mfma_f32_32x32x2_f32 on 32-wide
 //    hidden chunks of x and W_r staged through LDS (bf16 x widened exactly),
@@ -52,6 +53,10 @@ struct RouteArgs {
     int H, E, EP, K, NG, TG, G, EPL, LG, norm;
     float rsf;
 };
+
+// Sigmoid score of a logit, fp32; every router path uses this one expression
+// so that equal logits give equal scores whichever kernel computed them.
+__device__ __forceinline__ float sigmoid_score(float z) { return 1.0f / (1.0f + expf(-z)); }
 
 // Order-preserving map of an fp32 value to uint32 (larger float -> larger key).
 __device__ __forceinline__ uint32_t fkey(float f) {
@@ -285,7 +290,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
         for (int q = 0; q < 4; ++q) {
             if (q < EPL && lane_has && e0 + q < E) {
                 const float z = zs[r * ZLD + e0 + q];
-                s[q] = 1.0f / (1.0f + expf(-z));
+                s[q] = sigmoid_score(z);
                 c[q] = s[q] + bias_l[q];
             } else {
                 s[q] = 0.f;
@@ -337,18 +342,26 @@ struct RouteV2Args {
     float rsf;
 };
 
+// The exact three-plane split of one fp32 router weight: hi = RNE(w),
+// mid = RNE(w - hi), lo = RNE(w - hi - mid), with hi + mid + lo == w.  Every
+// router path takes its planes from this one routine.
+__device__ __forceinline__ void split3(float w, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
+    hi = f32_to_bf16(w);
+    const float r1 = w - bf16_to_f32(hi);
+    mid = f32_to_bf16(r1);
+    const float r2 = r1 - bf16_to_f32(mid);
+    lo = f32_to_bf16(r2);
+}
+
 __global__ __launch_bounds__(256) void router_split_kernel(const float* wr, uint16_t* planes,
                                                            int64_t n) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     if (i >= n) return;
-    const float w = wr[i];
-    const uint16_t hi = f32_to_bf16(w);
-    const float r1 = w - bf16_to_f32(hi);
-    const uint16_t mid = f32_to_bf16(r1);
-    const float r2 = r1 - bf16_to_f32(mid);
+    uint16_t hi, mid, lo;
+    split3(wr[i], hi, mid, lo);
     planes[i] = hi;
     planes[n + i] = mid;
-    planes[2 * n + i] = f32_to_bf16(r2);
+    planes[2 * n + i] = lo;
 }
 
 // 128-byte rows: chunk c of row r at c ^ ((r >> 1) & 7) (conflict-free reads)
@@ -660,7 +673,7 @@ __global__ __launch_bounds__(512) void route_bf16_kernel(RouteV2Args a) {
                 const int e0 = et * 32 + 8 * q + 4 * kh;
                 float sv[4];
 #pragma unroll
-                for (int p = 0; p < 4; ++p) sv[p] = 1.0f / (1.0f + expf(-acc[i][4 * q + p]));
+                for (int p = 0; p < 4; ++p) sv[p] = sigmoid_score(acc[i][4 * q + p]);
                 *reinterpret_cast<float4*>(Ss + tok * PITCH + e0) = make_float4(sv[0], sv[1], sv[2], sv[3]);
             }
         }
@@ -678,40 +691,43 @@ __global__ __launch_bounds__(512) void route_bf16_kernel(RouteV2Args a) {
 
 
 // ---------------------------------------------------------------------------
-// Few tokens (T <= RS_TMAX): the logits are split over workgroups along the
-// hidden dimension as well (RS_SPLIT parts), so that short batches fill the
-// chip instead of a few workgroups each walking all of H.  Partial logits go
-// to the workspace; a second kernel adds them in a fixed order, then scores
-// and routes each token with one wave.
+// Few tokens (T <= RS_TMAX): one workgroup per 32 tokens and 32 experts, so
+// that short batches spread over many CUs.  The logits are formed in exactly
+// the order route_bf16_kernel uses: two accumulator chains, one over the
+// 16-deep slices 0-1 and one over slices 2-3 of every 64-wide hidden k-tile,
+// each applying the three planes in order, then one fp32 add of the two.  So
+// a token's logits, and with them its routing, do not depend on how many
+// tokens share the call.  A 4-deep ring of k-tiles keeps the walk over the
+// hidden dimension ahead of the matrix cores.  The logits go to the
+// workspace; a second kernel scores and routes each token with one wave.
 // ---------------------------------------------------------------------------
-constexpr int RS_SPLIT = 4;
 constexpr int RS_TMAX = 4096;
+constexpr int RS_STAGES = 4;
 
-// grid: (ceil(T / 128), EP / 32, RS_SPLIT); 4 waves, wave w owns token tile w
-// against expert tile blockIdx.y (3 planes), hidden k-tiles of part blockIdx.z.
+// grid: (ceil(T / 32), EP / 32); 2 waves, wave w accumulates slices 2w and
+// 2w + 1 of every k-tile for 32 tokens x expert tile blockIdx.y (3 planes).
 template <int EP>
-__global__ __launch_bounds__(256) void route_logits_kernel(RouteV2Args a, float* zpart) {
+__global__ __launch_bounds__(128) void route_logits_kernel(RouteV2Args a, float* zout) {
     typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
     typedef float f32x16 __attribute__((ext_vector_type(16)));
     constexpr int BK = RV_BK;
-    constexpr int TOK = 128, WR = 96, ROWS = TOK + WR;  // x rows, plane rows (3 x 32 experts)
-    constexpr int STAGE = ROWS * BK;
-    constexpr int CI = ROWS / 4 / 8;                    // copies per wave per k-tile (8 rows each)
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE];
+    constexpr int TOK = 32, WR = 96, ROWS = TOK + WR;   // x rows, plane rows (3 x 32 experts)
+    constexpr int STAGE = ROWS * BK;                    // bf16 elements per stage (16 KB)
+    constexpr int CI = ROWS / 2 / 8;                    // copies per wave per k-tile (8 rows each)
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[RS_STAGES * STAGE];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TOK;
-    const int et = blockIdx.y, part = blockIdx.z;
+    const int et = blockIdx.y;
     const int H = a.H, E = a.E;
     const int nk = H / BK;
-    const int kt0 = nk * part / RS_SPLIT, kt1 = nk * (part + 1) / RS_SPLIT;
 
-    // copy i of wave w: stage rows w*ROWS/4 + 8i + lane/8 (x rows first, then
+    // copy i of wave w: stage rows w*ROWS/2 + 8i + lane/8 (x rows first, then
     // plane rows p*32 + e of expert tile et); chunk (lane%8) ^ rswz(row)
     const uint16_t* src[CI];
 #pragma unroll
     for (int i = 0; i < CI; ++i) {
-        const int r = wave * (ROWS / 4) + i * 8 + (lane >> 3);
+        const int r = wave * (ROWS / 2) + i * 8 + (lane >> 3);
         const int c = (lane & 7) ^ rswz(r);
         if (r < TOK) {
             int64_t t = t0 + r;
@@ -724,26 +740,30 @@ __global__ __launch_bounds__(256) void route_logits_kernel(RouteV2Args a, float*
             src[i] = a.planes + (static_cast<int64_t>(p) * E + e) * H + c * 8;
         }
     }
-    auto issue = [&](int kt, int s) {
-        const uint32_t base = lds_addr(smem + s * STAGE + wave * (ROWS / 4) * BK);
+    auto issue = [&](int kt) {
+        const uint32_t base = lds_addr(smem + (kt % RS_STAGES) * STAGE + wave * (ROWS / 2) * BK);
 #pragma unroll
         for (int i = 0; i < CI; ++i) lds_dma16(src[i] + kt * BK, base + i * 8 * BK * 2);
     };
     const int kh = lane >> 5, rl = lane & 31;
     f32x16 acc = f32x16{};
-    if (kt0 < kt1) issue(kt0, 0);
-    for (int kt = kt0; kt < kt1; ++kt) {
-        const int s = (kt - kt0) & 1;
-        wait_vmcnt<0>();
-        wait_lgkmcnt0();
-        block_barrier();                                // k-tile kt landed; stage 1 - s free
-        if (kt + 1 < kt1) issue(kt + 1, 1 - s);
-        const uint16_t* st = smem + s * STAGE;
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            const int ch = kk * 2 + kh;
-            const int rx = wave * 32 + rl;
-            const bf16x8 xf = *reinterpret_cast<const bf16x8*>(st + rx * BK + ((ch ^ rswz(rx)) * 8));
+    for (int j = 0; j < RS_STAGES - 1; ++j)
+        if (j < nk) issue(j);
+    for (int kt = 0; kt < nk; ++kt) {
+        // k-tile kt landed (the copies of up to two later k-tiles may be in flight)
+        const int later = nk - 1 - kt < RS_STAGES - 2 ? nk - 1 - kt : RS_STAGES - 2;
+        if (later >= 2) wait_vmcnt<2 * CI>();
+        else if (later == 1) wait_vmcnt<CI>();
+        else wait_vmcnt<0>();
+        wait_lgkmcnt0();
+        block_barrier();                                // every wave done with k-tile kt - 1
+        if (kt + RS_STAGES - 1 < nk) issue(kt + RS_STAGES - 1);
+        const uint16_t* st = smem + (kt % RS_STAGES) * STAGE;
+#pragma unroll
+        for (int ss = 0; ss < 2; ++ss) {
+            const int ch = (2 * wave + ss) * 2 + kh;
+            const bf16x8 xf = *reinterpret_cast<const bf16x8*>(st + rl * BK + ((ch ^ rswz(rl)) * 8));
 #pragma unroll
             for (int p = 0; p < 3; ++p) {
                 const int rw = TOK + p * 32 + rl;
@@ -752,10 +772,22 @@ __global__ __launch_bounds__(256) void route_logits_kernel(RouteV2Args a, float*
             }
         }
     }
-    // lane holds experts et*32 + 8q + 4*kh + [0, 4) of token t0 + 32 w + rl
-    const int64_t t = t0 + wave * 32 + rl;
+    // the two chains meet: logit = (slices 0-1) + (slices 2-3)
+    wait_lgkmcnt0();
+    block_barrier();
+    float* part = reinterpret_cast<float*>(smem);       // [16][64]
+    if (wave == 1) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) part[v * 64 + lane] = acc[v];
+    }
+    __syncthreads();
+    if (wave == 1) return;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] += part[v * 64 + lane];
+    // lane holds experts et*32 + 8q + 4*kh + [0, 4) of token t0 + rl
+    const int64_t t = t0 + rl;
     if (t < a.T) {
-        float* zrow = zpart + (static_cast<int64_t>(part) * a.T + t) * EP + et * 32;
+        float* zrow = zout + t * EP + et * 32;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             *reinterpret_cast<float4*>(zrow + 8 * q + 4 * kh) =
@@ -763,9 +795,8 @@ __global__ __launch_bounds__(256) void route_logits_kernel(RouteV2Args a, float*
     }
 }
 
-// grid: ceil(T / 4); 4 waves, one token each: the parts of the logits added
-// in a fixed order, then scores and routing by the wave.
-__global__ __launch_bounds__(256) void route_select_kernel(RouteV2Args a, const float* zpart,
+// grid: ceil(T / 4); 4 waves, one token each: scores and routing by the wave.
+__global__ __launch_bounds__(256) void route_select_kernel(RouteV2Args a, const float* z,
                                                            int EP, int EPL, int LG) {
     const int lane = threadIdx.x & 63;
     const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -778,10 +809,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteV2Args a, const 
         c[q] = -INFINITY;
         const int e = e0 + q;
         if (q < EPL && e < a.E) {
-            float z = 0.f;
-#pragma unroll
-            for (int pp = 0; pp < RS_SPLIT; ++pp) z += zpart[(static_cast<int64_t>(pp) * a.T + t) * EP + e];
-            s[q] = 1.0f / (1.0f + expf(-z));
+            s[q] = sigmoid_score(z[t * EP + e]);
             c[q] = s[q] + a.bias[e];
         }
     }
@@ -803,7 +831,7 @@ static size_t route_planes_bytes(const Dims& d) {
 size_t route_ws_bytes(const Dims& d) {
     if (!route_bf16_path(d)) return 0;
     const int EP = d.E <= 64 ? 64 : 128;
-    return route_planes_bytes(d) + static_cast<size_t>(RS_SPLIT) * RS_TMAX * EP * sizeof(float);
+    return route_planes_bytes(d) + static_cast<size_t>(RS_TMAX) * EP * sizeof(float);
 }
 
 hipError_t launch_route(const Dims& d, const void* x, const float* router_w, const float* e_bias,
@@ -833,16 +861,17 @@ hipError_t launch_route(const Dims& d, const void* x, const float* router_w, con
         a.norm = d.norm;
         a.rsf = d.rsf;
         if (d.T <= RS_TMAX) {
-            // few tokens: hidden-dimension split, then a scoring and routing pass
-            float* zpart = reinterpret_cast<float*>(static_cast<char*>(ws) + route_planes_bytes(d));
-            const unsigned nt = static_cast<unsigned>((d.T + 127) / 128);   // logits: 128-token tiles
+            // few tokens: logits over many small workgroups, then a scoring
+            // and routing pass
+            float* z = reinterpret_cast<float*>(static_cast<char*>(ws) + route_planes_bytes(d));
+            const unsigned nt = static_cast<unsigned>((d.T + 31) / 32);
             const int EP = d.E <= 64 ? 64 : 128;
             if (EP == 64)
-                hipLaunchKernelGGL(route_logits_kernel<64>, dim3(nt, 2, RS_SPLIT), dim3(256), 0, stream, a, zpart);
+                hipLaunchKernelGGL(route_logits_kernel<64>, dim3(nt, 2), dim3(128), 0, stream, a, z);
             else
-                hipLaunchKernelGGL(route_logits_kernel<128>, dim3(nt, 4, RS_SPLIT), dim3(256), 0, stream, a, zpart);
+                hipLaunchKernelGGL(route_logits_kernel<128>, dim3(nt, 4), dim3(128), 0, stream, a, z);
             hipLaunchKernelGGL(route_select_kernel, dim3(static_cast<unsigned>((d.T + 3) / 4)), dim3(256), 0,
-                               stream, a, zpart, EP, d.EPL, d.LG);
+                               stream, a, z, EP, d.EPL, d.LG);
             return hipGetLastError();
         }
         // tokens per workgroup: the fewest (32 TM, TM = 4..6) whose grid fits

@@ -33,7 +33,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "by_name", "make_inputs", "round_to_bf16",
-    "bf16_bits", "bits_to_f32", "digest", "token_mask",
+    "bf16_bits", "bits_to_f32", "digest", "token_mask", "random_act",
 ]
 
 
@@ -76,6 +76,13 @@ class Workload:
 
 
 _HOT8 = (0, 1, 2, 3, 32, 33, 34, 35)   # 8 experts spread over 2 of the 4 groups
+# With the correction bias of std 0.5, the +2.0 logit shift on _HOT8 puts only
+# ~26% of assignments on them: the bias is a fixed per-expert offset, and only
+# two of them have a bias high enough to win once their sigmoid saturates.
+# This set holds, for seed 4 at 38,000 tokens (the bias is drawn after x, so
+# its values depend on the token count), the four experts of largest bias in
+# each of groups 0 and 1; the same +2.0 shift then puts ~50% on them.
+_HOT8_HALF = (7, 18, 28, 31, 33, 34, 38, 39)
 
 WORKLOADS = (
     Workload("tiny_fp32_T64", T=64, hidden=256, num_experts=16, n_group=4, topk_group=2,
@@ -93,6 +100,9 @@ WORKLOADS = (
     Workload("hot_expert_T38000", T=38000, hidden=2048, num_experts=128, n_group=4,
              topk_group=2, top_k=8, intermediate=768, n_shared=1, dtype="bf16", seed=4,
              wr_std=2048 ** -0.5, b_std=0.5, hot=_HOT8, hot_shift=2.0),
+    Workload("hot_expert_half_T38000", T=38000, hidden=2048, num_experts=128, n_group=4,
+             topk_group=2, top_k=8, intermediate=768, n_shared=1, dtype="bf16", seed=4,
+             wr_std=2048 ** -0.5, b_std=0.5, hot=_HOT8_HALF, hot_shift=2.0),
 )
 
 
@@ -194,6 +204,13 @@ def make_inputs(wl: Workload, T: Optional[int] = None) -> dict:
     mask = token_mask(wl) if T == wl.T else None
     return dict(x=x, router_w=router_w, e_bias=e_bias, w13=w13, w2=w2,
                 shared_w13=shared_w13, shared_w2=shared_w2, mask=mask)
+
+
+def random_act(n: int, width: int, seed: int, std: float = 0.5) -> np.ndarray:
+    """A stand-in for gate/up activations (rows of the down projection's input):
+    float32 [n, width], N(0, std^2), rounded to bf16 values."""
+    a = _draw(np.random.default_rng(seed), (n, width), std)
+    return round_to_bf16(a)
 
 
 def digest(inputs: dict) -> dict:

@@ -21,7 +21,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     assert set(names) == set(lbv.EXPORTS)
     L = ctypes.CDLL(lbv.LIB_PATH)
     for n in names:
@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert lbv.lbv_abi_version() == 1
+    assert lbv.lbv_abi_version() == 2
     texts = {lbv.lbv_status_string(s) for s in range(8)}
     assert len(texts) == 8
     assert lbv.lbv_status_string(99) == "unknown status"
@@ -108,6 +108,14 @@ def test_bf16_offset_limits():
     with pytest.raises(lbv.LbvError) as e:
         lbv.lbv_moe_permute_workspace_size(small_h, 1 << 24)
     assert e.value.status == lbv.LBV_ERR_SHAPE
+    # the down matmul addresses a segment's act rows (up to T) with 32-bit offsets
+    tall = lbv.config(hidden=64, intermediate=1 << 14, num_experts=8, n_group=2, topk_group=1,
+                      top_k=2)
+    Tact = (1 << 32) // ((1 << 14) * 2)
+    assert lbv.lbv_moe_permute_workspace_size(tall, Tact - 1) > 0
+    with pytest.raises(lbv.LbvError) as e:
+        lbv.lbv_moe_permute_workspace_size(tall, Tact)
+    assert e.value.status == lbv.LBV_ERR_SHAPE
     wide = dict(hidden=1 << 15, intermediate=1 << 14, n_shared_experts=2)   # shared_w13 4 GiB
     assert lbv.lbv_moe_check_config(lbv.config(**wide)) == lbv.LBV_ERR_SHAPE
     assert lbv.lbv_moe_check_config(lbv.config(**dict(wide, n_shared_experts=1))) == lbv.LBV_OK
@@ -127,9 +135,9 @@ def test_route_validation_paths():
     c = lbv.config()
     L = raw()
     need = lbv.lbv_moe_route_workspace_size(c)
-    # three bf16 planes of W_r, then partial logits of the few-token path
-    # (4 hidden-dimension parts x 4096 tokens x 128 experts, fp32)
-    assert need == 3 * 128 * 2048 * 2 + 4 * 4096 * 128 * 4
+    # three bf16 planes of W_r, then the logits of the few-token path
+    # (4096 tokens x 128 experts, fp32)
+    assert need == 3 * 128 * 2048 * 2 + 4096 * 128 * 4
 
     def r(T, x, wr, b, ids, w, ws=Cc, nbytes=need):
         return L.lbv_moe_route(ctypes.byref(c), T, x, wr, b, None, ids, w, ws, nbytes, None)
@@ -173,10 +181,16 @@ def test_split_call_validation_paths():
     assert L.lbv_moe_permute(ctypes.byref(c), 8, A, None, B, B, Cc, BIG, None) == lbv.LBV_ERR_NULL
     assert L.lbv_moe_permute(ctypes.byref(c), 8, A, B, B, B, Cc, 0, None) == lbv.LBV_ERR_WORKSPACE
     assert L.lbv_moe_permute(ctypes.byref(c), 0, None, None, None, None, None, 0, None) == lbv.LBV_OK
-    assert L.lbv_moe_gemm_w13_silu(ctypes.byref(c), 8, A, B, None, B, B, Cc, None) == \
+    gw = lbv.lbv_moe_w13_workspace_size(c, 8)
+    assert gw == 256
+    assert L.lbv_moe_gemm_w13_silu(ctypes.byref(c), 8, A, B, None, B, B, Cc, Cc, gw, None) == \
         lbv.LBV_ERR_NULL
-    assert L.lbv_moe_gemm_w13_silu(ctypes.byref(c), 8, A, B + 2, A, B, B, Cc, None) == \
+    assert L.lbv_moe_gemm_w13_silu(ctypes.byref(c), 8, A, B, A, B, B, Cc, None, gw, None) == \
+        lbv.LBV_ERR_NULL
+    assert L.lbv_moe_gemm_w13_silu(ctypes.byref(c), 8, A, B + 2, A, B, B, Cc, Cc, gw, None) == \
         lbv.LBV_ERR_ALIGN
+    assert L.lbv_moe_gemm_w13_silu(ctypes.byref(c), 8, A, B, A, B, B, Cc, Cc, gw - 1, None) == \
+        lbv.LBV_ERR_WORKSPACE
     assert L.lbv_moe_gemm_w2_combine(ctypes.byref(c), 8, A, B, A, B, B, B, B, Cc, Cc, 0, None) == \
         lbv.LBV_ERR_WORKSPACE
     assert L.lbv_moe_gemm_w2_combine(ctypes.byref(c), 8, A, B, A, B, B, B, B, Cc, None, BIG,
@@ -191,3 +205,97 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(ValueError):
         lbv.lbv_moe_route(c, x, torch.zeros(8, 64), torch.zeros(8), None,
                           torch.zeros(4, 2, dtype=torch.int32), torch.zeros(4, 2))
+
+
+def small_cfg(**kw):
+    base = dict(hidden=64, intermediate=64, num_experts=8, n_group=2, topk_group=1, top_k=2,
+                n_shared_experts=1)
+    base.update(kw)
+    return lbv.config(**base)
+
+
+def host_block(c, T=4):
+    """Host tensors with the shapes the calls expect (the binding checks shapes
+    before it looks at devices, so wrong shapes are reported on the CPU)."""
+    import torch
+    H, E, K, I, ns = c.hidden, c.num_experts, c.top_k, c.intermediate, c.n_shared_experts
+    KS, S = K + ns, E + ns
+    return dict(x=torch.zeros(T, H, dtype=torch.bfloat16), router_w=torch.zeros(E, H),
+                e_bias=torch.zeros(E), mask=torch.ones(T, dtype=torch.uint8),
+                w13=torch.zeros(E, 2 * I, H, dtype=torch.bfloat16),
+                w2=torch.zeros(E, H, I, dtype=torch.bfloat16),
+                shared_w13=torch.zeros(2 * I * ns, H, dtype=torch.bfloat16),
+                shared_w2=torch.zeros(H, I * ns, dtype=torch.bfloat16),
+                out=torch.zeros(T, H, dtype=torch.bfloat16),
+                ids=torch.zeros(T, K, dtype=torch.int32), w=torch.zeros(T, K),
+                off=torch.zeros(S + 1, dtype=torch.int32),
+                srt=torch.zeros(T * KS, dtype=torch.int32),
+                inv=torch.zeros(T * KS, dtype=torch.int32),
+                act=torch.zeros(T * KS, I, dtype=torch.bfloat16),
+                ws=torch.zeros(1 << 16, dtype=torch.uint8))
+
+
+def call(name, c, b):
+    if name == "forward":
+        lbv.lbv_moe_forward(c, b["x"], b["mask"], b["router_w"], b["e_bias"], b["w13"], b["w2"],
+                            b["shared_w13"], b["shared_w2"], b["out"], b["ids"], b["w"], b["ws"])
+    elif name == "route":
+        lbv.lbv_moe_route(c, b["x"], b["router_w"], b["e_bias"], b["mask"], b["ids"], b["w"],
+                          b["ws"])
+    elif name == "permute":
+        lbv.lbv_moe_permute(c, b["ids"], b["off"], b["srt"], b["inv"], b["ws"])
+    elif name == "w13":
+        lbv.lbv_moe_gemm_w13_silu(c, b["x"], b["w13"], b["shared_w13"], b["off"], b["srt"],
+                                  b["act"], b["ws"])
+    else:
+        lbv.lbv_moe_gemm_w2_combine(c, b["act"], b["w2"], b["shared_w2"], b["off"], b["srt"],
+                                    b["inv"], b["w"], b["out"], b["ws"])
+
+
+WRONG = [
+    ("forward", "x", (4, 128)), ("forward", "mask", (5,)), ("forward", "router_w", (8, 32)),
+    ("forward", "e_bias", (7,)), ("forward", "w13", (8, 64, 64)), ("forward", "w2", (8, 64, 32)),
+    ("forward", "shared_w13", (64, 64)), ("forward", "shared_w2", (64, 128)),
+    ("forward", "out", (3, 64)), ("forward", "ids", (4, 3)), ("forward", "w", (4, 1)),
+    ("route", "x", (4, 32)), ("route", "ids", (5, 2)), ("route", "w", (4, 3)),
+    ("route", "router_w", (9, 64)), ("route", "mask", (3,)),
+    ("permute", "ids", (4, 3)), ("permute", "off", (9,)), ("permute", "srt", (11,)),
+    ("permute", "inv", (11,)),
+    ("w13", "w13", (8, 128, 32)), ("w13", "shared_w13", (128, 32)), ("w13", "act", (11, 64)),
+    ("w13", "act", (12, 32)), ("w13", "srt", (11,)), ("w13", "off", (9,)),
+    ("w2", "w2", (8, 32, 64)), ("w2", "shared_w2", (32, 64)), ("w2", "w", (5, 2)),
+    ("w2", "out", (4, 32)), ("w2", "act", (11, 64)), ("w2", "inv", (11,)),
+]
+
+
+@pytest.mark.parametrize("name,key,shape", WRONG)
+def test_binding_rejects_wrong_shapes(name, key, shape):
+    """A mis-shaped tensor is refused before any pointer reaches the library."""
+    import torch
+    c = small_cfg()
+    b = host_block(c)
+    b[key] = torch.zeros(*shape, dtype=b[key].dtype)
+    with pytest.raises(ValueError) as e:
+        call(name, c, b)
+    assert "shape" in str(e.value) or "elements" in str(e.value)
+
+
+@pytest.mark.parametrize("name", ["forward", "route", "permute", "w13", "w2"])
+def test_binding_right_shapes_reach_the_device_check(name):
+    """With every shape right, the only complaint left is that the tensors are
+    on the host."""
+    c = small_cfg()
+    with pytest.raises(ValueError) as e:
+        call(name, c, host_block(c))
+    assert "device tensor" in str(e.value)
+
+
+def test_binding_rejects_shared_weights_without_shared_expert():
+    c = small_cfg(n_shared_experts=0)
+    b = host_block(small_cfg())
+    b["srt"] = b["srt"][:8]
+    b["inv"] = b["inv"][:8]
+    b["act"] = b["act"][:8]
+    with pytest.raises(ValueError) as e:
+        call("w13", c, b)
+    assert "n_shared_experts" in str(e.value)
