@@ -63,7 +63,8 @@ typedef enum {
     LBV_ERR_ALIAS = 4,        /* out overlaps x (the block is not in-place)        */
     LBV_ERR_ALIGN = 5,        /* a pointer is not 16-byte aligned                 */
     LBV_ERR_WORKSPACE = 6,    /* ws_bytes smaller than the size query returns     */
-    LBV_ERR_HIP = 7           /* a kernel launch failed                           */
+    LBV_ERR_HIP = 7,          /* a kernel launch failed                           */
+    LBV_ERR_SCRATCH = 8       /* an allocation-free call's fixed scratch is too small */
 } lbv_status;
 
 typedef enum { LBV_F32 = 0, LBV_BF16 = 1 } lbv_dtype;
@@ -150,6 +151,25 @@ lbv_status lbv_moe_route(const lbv_moe_config *cfg, int64_t T, const void *x,
                          const float *router_w, const float *e_bias, const uint8_t *mask,
                          int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes,
                          hipStream_t stream);
+
+/*
+ * Allocation-free router, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, results and errors as lbv_moe_route, minus
+ * the workspace: its scratch is a fixed 8 MiB device array inside the library
+ * (one per GPU, held until the process ends), so the call needs
+ * lbv_moe_route_workspace_size(cfg) <= 8 MiB (3 E H bf16 planes plus
+ * 4096 x 128 fp32 logits; H up to about 8192 with 128 experts), else
+ * LBV_ERR_SCRATCH.  It allocates nothing; its first call on a device looks up
+ * the array's address there (LBV_ERR_HIP if that fails).  Every call on a
+ * GPU shares that GPU's array: calls that overlap in time on one GPU (other
+ * host threads, other streams) race and must be serialised by the caller.
+ * Nothing in the array needs to start at zero.
+ */
+lbv_status lbv_moe_route_noalloc(const lbv_moe_config *cfg, int64_t T, const void *x,
+                                 const float *router_w, const float *e_bias,
+                                 const uint8_t *mask, int32_t *topk_ids, float *topk_w,
+                                 hipStream_t stream);
 
 /*
  * Token-to-expert permutation (vLLM-Omni article, "MoE 实现的源码级要点":

@@ -19,7 +19,8 @@ __all__ = [
     "LbvError", "MoEConfig", "config", "load", "lbv_abi_version", "lbv_status_string",
     "lbv_moe_check_config", "lbv_moe_workspace_size", "lbv_moe_route_workspace_size",
     "lbv_moe_permute_workspace_size", "lbv_moe_w13_workspace_size",
-    "lbv_moe_w2_workspace_size", "lbv_moe_route", "lbv_moe_permute", "lbv_moe_gemm_w13_silu",
+    "lbv_moe_w2_workspace_size", "lbv_moe_route", "lbv_moe_route_noalloc", "lbv_moe_permute",
+    "lbv_moe_gemm_w13_silu",
     "lbv_moe_gemm_w2_combine", "lbv_moe_forward", "EXPORTS", "LIB_PATH",
 ]
 
@@ -28,13 +29,14 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblbv_moe.
 # status codes of lbv_moe.h
 LBV_OK, LBV_ERR_NULL, LBV_ERR_SHAPE, LBV_ERR_UNSUPPORTED = 0, 1, 2, 3
 LBV_ERR_ALIAS, LBV_ERR_ALIGN, LBV_ERR_WORKSPACE, LBV_ERR_HIP = 4, 5, 6, 7
+LBV_ERR_SCRATCH = 8
 LBV_F32, LBV_BF16 = 0, 1
 LBV_SCORE_SIGMOID, LBV_SCORE_SOFTMAX = 0, 1
 
 EXPORTS = (
     "lbv_abi_version", "lbv_status_string", "lbv_moe_check_config", "lbv_moe_workspace_size",
     "lbv_moe_route_workspace_size", "lbv_moe_permute_workspace_size", "lbv_moe_w13_workspace_size",
-    "lbv_moe_w2_workspace_size", "lbv_moe_route",
+    "lbv_moe_w2_workspace_size", "lbv_moe_route", "lbv_moe_route_noalloc",
     "lbv_moe_permute", "lbv_moe_gemm_w13_silu", "lbv_moe_gemm_w2_combine", "lbv_moe_forward",
 )
 
@@ -103,6 +105,8 @@ def load():
     L.lbv_moe_route_workspace_size.restype = st
     L.lbv_moe_route.argtypes = [C, I64, P, P, P, P, P, P, P, SZ, P]
     L.lbv_moe_route.restype = st
+    L.lbv_moe_route_noalloc.argtypes = [C, I64, P, P, P, P, P, P, P]
+    L.lbv_moe_route_noalloc.restype = st
     L.lbv_moe_permute.argtypes = [C, I64, P, P, P, P, P, SZ, P]
     L.lbv_moe_permute.restype = st
     L.lbv_moe_gemm_w13_silu.argtypes = [C, I64, P, P, P, P, P, P, P, SZ, P]
@@ -247,6 +251,26 @@ def lbv_moe_route(cfg, x, router_w, e_bias, mask, topk_ids, topk_w, ws=None, str
         _ptr(topk_ids, "topk_ids", torch.int32), _ptr(topk_w, "topk_w", torch.float32),
         _ptr(ws, "ws"), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
         "lbv_moe_route")
+
+
+def lbv_moe_route_noalloc(cfg, x, router_w, e_bias, mask, topk_ids, topk_w, stream=None):
+    """lbv_moe_route with the library's fixed per-GPU scratch instead of a
+    workspace (allocates nothing; overlapping calls on one GPU race)."""
+    dt = cfg.torch_dtype
+    H, E, K, I, ns, KS, S = _dims(cfg)
+    _shape(x, "x", None, H)
+    T = x.shape[0]
+    _shape(router_w, "router_w", E, H)
+    _shape(e_bias, "e_bias", E)
+    _shape(mask, "mask", T)
+    _shape(topk_ids, "topk_ids", T, K)
+    _shape(topk_w, "topk_w", T, K)
+    _same_device(x, router_w, e_bias, mask, topk_ids, topk_w)
+    _check(load().lbv_moe_route_noalloc(
+        ctypes.byref(cfg), T, _ptr(x, "x", dt), _ptr(router_w, "router_w", torch.float32),
+        _ptr(e_bias, "e_bias", torch.float32), _ptr(mask, "mask", torch.uint8),
+        _ptr(topk_ids, "topk_ids", torch.int32), _ptr(topk_w, "topk_w", torch.float32),
+        _stream(stream)), "lbv_moe_route_noalloc")
 
 
 def lbv_moe_permute(cfg, topk_ids, offsets, sorted_rows, inv_rows, ws, stream=None):

@@ -146,6 +146,8 @@ const char* lbv_status_string(lbv_status s) {
         case LBV_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case LBV_ERR_WORKSPACE: return "workspace smaller than the size query returns";
         case LBV_ERR_HIP: return "a HIP kernel launch failed";
+        case LBV_ERR_SCRATCH:
+            return "the allocation-free call's fixed scratch is too small for this configuration";
     }
     return "unknown status";
 }
@@ -213,6 +215,24 @@ lbv_status lbv_moe_route(const lbv_moe_config* cfg, int64_t T, const void* x,
         return LBV_ERR_ALIGN;
     if (ws_bytes < need) return LBV_ERR_WORKSPACE;
     return hip_status(lbv::launch_route(d, x, router_w, e_bias, mask, topk_ids, topk_w, ws, stream));
+}
+
+lbv_status lbv_moe_route_noalloc(const lbv_moe_config* cfg, int64_t T, const void* x,
+                                 const float* router_w, const float* e_bias, const uint8_t* mask,
+                                 int32_t* topk_ids, float* topk_w, hipStream_t stream) {
+    Dims d;
+    lbv_status st = make_dims(cfg, T, &d);
+    if (st != LBV_OK) return st;
+    if (T == 0) return LBV_OK;
+    if (!x || !router_w || !e_bias || !topk_ids || !topk_w) return LBV_ERR_NULL;
+    if (!aligned16(x) || !aligned16(router_w) || !aligned4(e_bias) || !aligned4(topk_ids) ||
+        !aligned4(topk_w))
+        return LBV_ERR_ALIGN;
+    if (round_up(lbv::route_ws_bytes(d)) > lbv::kRouteScratchBytes) return LBV_ERR_SCRATCH;
+    void* scratch = nullptr;
+    if (lbv::route_scratch(&scratch) != hipSuccess) return LBV_ERR_HIP;
+    return hip_status(lbv::launch_route(d, x, router_w, e_bias, mask, topk_ids, topk_w, scratch,
+                                        stream));
 }
 
 lbv_status lbv_moe_permute(const lbv_moe_config* cfg, int64_t T, const int32_t* topk_ids,

@@ -53,6 +53,12 @@ hipError_t launch_route(const Dims& d, const void* x, const float* router_w, con
                         const uint8_t* mask, int32_t* topk_ids, float* topk_w, void* ws,
                         hipStream_t stream);
 
+// Allocation-free router: the fixed per-device scratch (the router
+// workspace must fit in it) and its device address on the current device.
+constexpr size_t kRouteScratchBytes = size_t(8) << 20;
+constexpr int kMaxDevices = 64;
+hipError_t route_scratch(void** ptr);
+
 size_t permute_ws_bytes(const Dims& d);
 hipError_t launch_permute(const Dims& d, const int32_t* topk_ids, int32_t* offsets,
                           int32_t* sorted_rows, int32_t* inv_rows, void* ws,

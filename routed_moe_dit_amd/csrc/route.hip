@@ -28,8 +28,17 @@
 // repeated wave-wide arg-max reductions on 64-bit keys (order-preserving
 // score bits, inverted index), so ties go to the lower index exactly as in a
 // sequential scan.
+#include <mutex>
+
 #include "lbv_internal.h"
 #include "lbv_pipe.h"
+
+// Scratch of the allocation-free router entry (lbv_moe_route_noalloc): the
+// W_r planes and the few-token logits.  One copy per GPU, shared by every
+// call on that GPU; host code never uses this name as an address (it is a
+// host-side stand-in): route_scratch() looks up the device address once per
+// device with hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[lbv::kRouteScratchBytes];
 
 namespace lbv {
 namespace {
@@ -832,6 +841,24 @@ size_t route_ws_bytes(const Dims& d) {
     if (!route_bf16_path(d)) return 0;
     const int EP = d.E <= 64 ? 64 : 128;
     return route_planes_bytes(d) + static_cast<size_t>(RS_TMAX) * EP * sizeof(float);
+}
+
+hipError_t route_scratch(void** ptr) {
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {nullptr};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_route(const Dims& d, const void* x, const float* router_w, const float* e_bias,

@@ -21,7 +21,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     assert set(names) == set(lbv.EXPORTS)
     L = ctypes.CDLL(lbv.LIB_PATH)
     for n in names:
@@ -30,8 +30,8 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     assert lbv.lbv_abi_version() == 2
-    texts = {lbv.lbv_status_string(s) for s in range(8)}
-    assert len(texts) == 8
+    texts = {lbv.lbv_status_string(s) for s in range(9)}
+    assert len(texts) == 9
     assert lbv.lbv_status_string(99) == "unknown status"
 
 
@@ -299,3 +299,24 @@ def test_binding_rejects_shared_weights_without_shared_expert():
     with pytest.raises(ValueError) as e:
         call("w13", c, b)
     assert "n_shared_experts" in str(e.value)
+
+
+def test_route_noalloc_validation_paths():
+    """The allocation-free router rejects before touching the device: missing
+    pointers, misalignment, and a router scratch beyond its fixed 8 MiB."""
+    c = lbv.config()
+    L = raw()
+
+    def r(cfg, T, x=A, wr=A, b=B, ids=Cc, w=Cc):
+        return L.lbv_moe_route_noalloc(ctypes.byref(cfg), T, x, wr, b, None, ids, w, None)
+
+    assert r(c, 0) == lbv.LBV_OK
+    assert r(c, 4, x=None) == lbv.LBV_ERR_NULL
+    assert r(c, 4, w=None) == lbv.LBV_ERR_NULL
+    assert r(c, 4, x=A + 2) == lbv.LBV_ERR_ALIGN
+    # 3 x 128 x 16384 bf16 planes = 12 MiB > 8 MiB
+    big = lbv.config(hidden=16384)
+    assert lbv.lbv_moe_route_workspace_size(big) > (8 << 20)
+    assert r(big, 4) == lbv.LBV_ERR_SCRATCH
+    # the LingBot shape fits: 1.5 MiB of planes + 2 MiB of logits
+    assert lbv.lbv_moe_route_workspace_size(c) <= (8 << 20)
