@@ -197,6 +197,50 @@ def down_combine(wl, act_slots, ids, w, w2, shared_w2=None):
     return out
 
 
+def adaln_rmsnorm(x, temb6, table, eps=1e-6, round_bf16=True, per_token=True):
+    """h = rmsnorm(x) * (1 + scale) + shift (rows 4 and 3 of table + temb6),
+    fp64, rounded to bf16 when round_bf16.  x [n, H] fp32; temb6 [n, 6, H]
+    (per_token) or [6, H]; table [6, H].  Returns fp32 [n, H]."""
+    x, temb6, table = _f32(x), _f32(temb6), _f32(table)
+    n, H = x.shape
+    assert table.shape == (6, H)
+    assert temb6.shape == ((n, 6, H) if per_token else (6, H))
+    h = np.empty((n, H), np.float32)
+    L = lib()
+    L.orc_adaln_rmsnorm.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_int64, ctypes.c_void_p, ctypes.c_double, ctypes.c_int,
+                                    ctypes.c_void_p]
+    L.orc_adaln_rmsnorm.restype = None
+    L.orc_adaln_rmsnorm(H, n, _p(x), _p(temb6), 6 * H if per_token else 0, _p(table), float(eps),
+                        int(bool(round_bf16)), _p(h))
+    return h
+
+
+def bf16_round(values):
+    """Nearest bf16 value (ties to even) of each float64 value."""
+    v = np.ascontiguousarray(values, dtype=np.float64)
+    out = np.empty_like(v)
+    L = lib()
+    L.orc_bf16_round.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    L.orc_bf16_round.restype = None
+    L.orc_bf16_round(v.size, _p(v), _p(out))
+    return out
+
+
+def ffn_adaln(wl, x, temb6, table, router_w, e_bias, w13, w2, shared_w13=None, shared_w2=None,
+              mask=None, eps=1e-6, per_token=True):
+    """The FFN half of a DiT layer around the block:
+    out = x + gate * block(h), h = bf16(rmsnorm(x) (1 + scale) + shift),
+    gate = row 5 of table + temb6, all in fp64 from the fp32 inputs.
+    Returns dict(out fp64 [n, H], h fp32, block (the forward dict on h))."""
+    h = adaln_rmsnorm(x, temb6, table, eps, round_bf16=wl.dtype == "bf16", per_token=per_token)
+    blk = moe_forward(wl, h, router_w, e_bias, w13, w2, shared_w13, shared_w2, mask)
+    t6 = np.asarray(temb6, np.float64)
+    gate = np.asarray(table, np.float64)[5][None, :] + (t6[:, 5, :] if per_token else t6[5][None, :])
+    out = np.asarray(x, np.float64) + gate * blk["out"]
+    return dict(out=out, h=h, block=blk)
+
+
 def expert_act(wl, x_row, w13, e):
     """fp64 act [I] of routed expert e for one token."""
     x_row, w13 = _f32(x_row), _f32(w13)

@@ -432,6 +432,62 @@ void orc_down_combine(const orc_cfg *c, int64_t ntok, const float *act, const in
     }
 }
 
+/* ---------------------------------------------------------------------------
+ * The steps around the block in a DiT layer ([P1] step 2: AdaLN through
+ * scale_shift_table and a token-level temb6, fp32-sensitive modules
+ * including every norm; [P2] "MoE 实现的源码级要点": RMSNorm accumulates in
+ * fp32).  Readings (the pages give no formula): the FFN half of a layer is
+ *   out = x + gate * MoE(bf16(rmsnorm(x) * (1 + scale) + shift)),
+ * with (shift, scale, gate) = rows 3, 4, 5 of scale_shift_table[6, H] +
+ * temb6[t][6, H] (rows 0-2 belong to the attention half), RMSNorm
+ * x / sqrt(mean(x^2) + eps) with no learnable weight (the modulation is the
+ * affine part), the residual stream x in fp32, and the MoE input rounded once
+ * to the experts' storage type.
+ * ------------------------------------------------------------------------- */
+
+/* Nearest bf16 value of d (ties to even), computed from d directly: the
+ * 8 significant bits of the binary expansion of d, rounded by rint (the
+ * default rounding mode is to nearest, ties to even).  Normal range only. */
+static double bf16_round_d(double d)
+{
+    if (d == 0.0 || !isfinite(d)) return d;
+    int e;
+    const double m = frexp(d, &e);          /* d = m 2^e, 0.5 <= |m| < 1 */
+    return ldexp(rint(ldexp(m, 8)), e - 8);
+}
+
+/*
+ * h[t] = rmsnorm(x[t]) * (1 + scale[t]) + shift[t], fp64, then rounded to
+ * bf16 when round_bf16 (stored as fp32, exact).  x [ntok, H] fp32;
+ * temb6 row t at temb6 + t * temb_stride (6 H fp32 values; stride 0: one row
+ * for all tokens); table [6, H].
+ */
+void orc_adaln_rmsnorm(int H, int64_t ntok, const float *x, const float *temb6,
+                       int64_t temb_stride, const float *table, double eps, int round_bf16,
+                       float *h)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < ntok; ++t) {
+        const float *xt = x + t * H;
+        const float *et = temb6 + t * temb_stride;
+        double ss = 0.0;
+        for (int i = 0; i < H; ++i) ss += (double)xt[i] * (double)xt[i];
+        const double r = 1.0 / sqrt(ss / H + eps);
+        for (int i = 0; i < H; ++i) {
+            const double shift = (double)table[3 * H + i] + (double)et[3 * H + i];
+            const double scale = (double)table[4 * H + i] + (double)et[4 * H + i];
+            const double v = (double)xt[i] * r * (1.0 + scale) + shift;
+            h[t * H + i] = (float)(round_bf16 ? bf16_round_d(v) : v);
+        }
+    }
+}
+
+/* The nearest bf16 value of each double (exposed for its pin). */
+void orc_bf16_round(int64_t n, const double *in, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = bf16_round_d(in[i]);
+}
+
 /*
  * Token copies sorted by expert ([P2] "MoE 实现的源码级要点": tokens are
  * reordered by expert before the grouped matmuls and restored after).

@@ -33,7 +33,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "by_name", "make_inputs", "round_to_bf16",
-    "bf16_bits", "bits_to_f32", "digest", "token_mask", "random_act",
+    "bf16_bits", "bits_to_f32", "digest", "token_mask", "random_act", "make_adaln_inputs",
 ]
 
 
@@ -211,6 +211,21 @@ def random_act(n: int, width: int, seed: int, std: float = 0.5) -> np.ndarray:
     float32 [n, width], N(0, std^2), rounded to bf16 values."""
     a = _draw(np.random.default_rng(seed), (n, width), std)
     return round_to_bf16(a)
+
+
+def make_adaln_inputs(wl: Workload, T: Optional[int] = None, per_token: bool = True,
+                      x_std: float = 1.0, table_std: float = 0.1, temb_std: float = 0.1) -> dict:
+    """Inputs of the DiT layer's FFN half around the block (a stream of its
+    own, seed + 1000): the fp32 residual stream ``x [T, H]``, the modulation
+    table ``table [6, H]`` and the time embedding ``temb6`` ([T, 6, H] when
+    per_token, else [6, H]), all float32 N(0, std^2)."""
+    T = wl.T if T is None else T
+    H = wl.hidden
+    rng = np.random.default_rng(wl.seed + 1000)
+    x = _draw(rng, (T, H), x_std)
+    table = _draw(rng, (6, H), table_std)
+    temb6 = _draw(rng, (T, 6, H) if per_token else (6, H), temb_std)
+    return dict(x=x, table=table, temb6=temb6)
 
 
 def digest(inputs: dict) -> dict:
