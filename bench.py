@@ -47,6 +47,9 @@ def parse():
     p.add_argument("--cpu-sample", type=int, default=12000,
                    help="tokens of the same workload the CPU oracle is timed on")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--adaln", action="store_true",
+                   help="also time the FFN half of a DiT layer around the block "
+                        "(lbv_moe_ffn_adaln, token-level temb6) and its AdaLN kernel alone")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after the measurements, run a plain 1 GiB device copy three times, so "
                         "that a hardware-counter run can scale its byte counters")
@@ -272,6 +275,50 @@ def main():
     }
     if wl.hot:
         res["hot_expert_share"] = float(counts[list(wl.hot)].sum() / max(counts.sum(), 1))
+
+    # ---- the FFN half of a DiT layer around the block (AdaLN, gated residual) ------
+    if args.adaln:
+        ada = synth.make_adaln_inputs(wl, per_token=True)
+        xr = torch.from_numpy(ada["x"]).cuda()
+        temb = torch.from_numpy(ada["temb6"]).cuda()
+        table = torch.from_numpy(ada["table"]).cuda()
+        del ada
+        fout = torch.empty_like(xr)
+        fws = torch.empty(lbv.lbv_moe_ffn_adaln_workspace_size(cfg, T), dtype=torch.uint8,
+                          device="cuda")
+        hbuf = torch.empty(T, H, dtype=x.dtype, device="cuda")
+
+        def ffn():
+            lbv.lbv_moe_ffn_adaln(cfg, xr, mask, temb, table, 1e-6, router_w, e_bias, w13, w2,
+                                  sw13, sw2, fout, ids, wts, fws, stream)
+
+        def timed(fn, n):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+            e[0].record(stream)
+            for i in range(n):
+                fn()
+                e[i + 1].record(stream)
+            torch.cuda.synchronize()
+            return [e[i].elapsed_time(e[i + 1]) for i in range(n)]
+
+        f_ms = timed(ffn, max(10, args.steps // 2))
+        a_ms = timed(lambda: lbv.lbv_adaln_rmsnorm(cfg, xr, temb, table, 1e-6, hbuf, stream),
+                     max(10, args.steps // 2))
+        a_bytes = T * H * 4 + 2 * T * H * 4 + T * H * esz     # x, shift + scale rows, h
+        res["adaln"] = {
+            "ffn_adaln_ms": float(np.median(f_ms)),
+            "ffn_adaln_tokens_per_s": T / (float(np.median(f_ms)) * 1e-3),
+            "extra_over_block_ms": float(np.median(f_ms)) - pct(per_step, 50),
+            "adaln_kernel_ms": float(np.median(a_ms)),
+            "adaln_algorithmic_bytes": a_bytes,
+            "adaln_gbs": a_bytes / (float(np.median(a_ms)) * 1e-3) / 1e9,
+            "adaln_frac_hbm": a_bytes / (float(np.median(a_ms)) * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "temb6": "token-level [T, 6, H] fp32",
+        }
+        del temb, fws
 
     # ---- CPU oracle on a bounded sample of the same workload -----------------------
     if not args.no_cpu_baseline:

@@ -248,6 +248,53 @@ lbv_status lbv_moe_forward(const lbv_moe_config *cfg, int64_t T, const void *x,
                            const void *shared_w2, void *out, int32_t *topk_ids_out,
                            float *topk_w_out, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * ---------------------------------------------------------------------------
+ * The steps on either side of the block in a LingBot-Video DiT layer (prhub
+ * summary of sglang PR #32341, "实现拆解" step 2: AdaLN through
+ * scale_shift_table and a token-level temb6, the norms kept in fp32;
+ * vLLM-Omni article, "MoE 实现的源码级要点": RMSNorm accumulates in fp32).
+ * Reading taken (the pages give no formula): the FFN half of a layer is
+ *   out = x + gate * block(h),   h = rmsnorm(x) * (1 + scale) + shift,
+ *   rmsnorm(x) = x / sqrt(mean(x^2) + eps)   (no learnable weight),
+ *   (shift, scale, gate) = rows 3, 4, 5 of table + temb6 row t (fp32; rows
+ *   0-2 belong to the attention half),
+ * with x and out the fp32 residual stream and h rounded once to cfg->dtype.
+ *   x      [T, H]      fp32
+ *   temb6  6 H fp32 values per token at temb6 + t * temb_stride (elements,
+ *          a multiple of 4; 0 = one row for every token)
+ *   table  [6, H]      fp32 (scale_shift_table)
+ *   eps    >= 0, finite
+ * ---------------------------------------------------------------------------
+ */
+
+/* h [T, H] (cfg->dtype) = rmsnorm(x) * (1 + scale) + shift, rounded once;
+ * the sum of squares accumulates in fp32.  h must not overlap x. */
+lbv_status lbv_adaln_rmsnorm(const lbv_moe_config *cfg, int64_t T, const float *x,
+                             const float *temb6, int64_t temb_stride, const float *table,
+                             float eps, void *h, hipStream_t stream);
+
+/* Workspace of lbv_moe_ffn_adaln: lbv_moe_workspace_size plus h [T, H]. */
+lbv_status lbv_moe_ffn_adaln_workspace_size(const lbv_moe_config *cfg, int64_t T,
+                                            size_t *bytes);
+
+/*
+ * The FFN half of a DiT layer: h = AdaLN(x), the block on h (route, permute,
+ * gate/up + SiLU, down + combine), and the gated residual
+ *   out[t] = x[t] + gate[t] * (sum_k w[t,k] y[t,k] + shared y[t])
+ * formed in fp32 from the combine's fp32 sum (the block output is not
+ * rounded).  out [T, H] fp32 may be x itself (in place), but may not overlap
+ * it otherwise.  mask, router and expert weights, topk_ids_out / topk_w_out
+ * as in lbv_moe_forward; ws: lbv_moe_ffn_adaln_workspace_size bytes.
+ */
+lbv_status lbv_moe_ffn_adaln(const lbv_moe_config *cfg, int64_t T, const float *x,
+                             const uint8_t *mask, const float *temb6, int64_t temb_stride,
+                             const float *table, float eps, const float *router_w,
+                             const float *e_bias, const void *w13, const void *w2,
+                             const void *shared_w13, const void *shared_w2, float *out,
+                             int32_t *topk_ids_out, float *topk_w_out, void *ws, size_t ws_bytes,
+                             hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

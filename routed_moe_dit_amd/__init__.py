@@ -21,7 +21,8 @@ __all__ = [
     "lbv_moe_permute_workspace_size", "lbv_moe_w13_workspace_size",
     "lbv_moe_w2_workspace_size", "lbv_moe_route", "lbv_moe_route_noalloc", "lbv_moe_permute",
     "lbv_moe_gemm_w13_silu",
-    "lbv_moe_gemm_w2_combine", "lbv_moe_forward", "EXPORTS", "LIB_PATH",
+    "lbv_moe_gemm_w2_combine", "lbv_moe_forward", "lbv_adaln_rmsnorm",
+    "lbv_moe_ffn_adaln_workspace_size", "lbv_moe_ffn_adaln", "EXPORTS", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblbv_moe.so")
@@ -38,6 +39,7 @@ EXPORTS = (
     "lbv_moe_route_workspace_size", "lbv_moe_permute_workspace_size", "lbv_moe_w13_workspace_size",
     "lbv_moe_w2_workspace_size", "lbv_moe_route", "lbv_moe_route_noalloc",
     "lbv_moe_permute", "lbv_moe_gemm_w13_silu", "lbv_moe_gemm_w2_combine", "lbv_moe_forward",
+    "lbv_adaln_rmsnorm", "lbv_moe_ffn_adaln_workspace_size", "lbv_moe_ffn_adaln",
 )
 
 
@@ -115,6 +117,13 @@ def load():
     L.lbv_moe_gemm_w2_combine.restype = st
     L.lbv_moe_forward.argtypes = [C, I64, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     L.lbv_moe_forward.restype = st
+    F = ctypes.c_float
+    L.lbv_adaln_rmsnorm.argtypes = [C, I64, P, P, I64, P, F, P, P]
+    L.lbv_adaln_rmsnorm.restype = st
+    L.lbv_moe_ffn_adaln_workspace_size.argtypes = [C, I64, ctypes.POINTER(SZ)]
+    L.lbv_moe_ffn_adaln_workspace_size.restype = st
+    L.lbv_moe_ffn_adaln.argtypes = [C, I64, P, P, P, I64, P, F, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    L.lbv_moe_ffn_adaln.restype = st
     _lib = L
     return L
 
@@ -359,6 +368,72 @@ def lbv_moe_forward(cfg, x, mask, router_w, e_bias, w13, w2, shared_w13, shared_
         _ptr(topk_ids_out, "topk_ids_out", torch.int32),
         _ptr(topk_w_out, "topk_w_out", torch.float32), _ptr(ws, "ws"),
         ws.numel() * ws.element_size(), _stream(stream)), "lbv_moe_forward")
+
+
+def _temb_rows(temb6, T, H):
+    """(pointer tensor, row stride in elements) of a token-level [T, 6, H] or a
+    shared [6, H] time embedding."""
+    if temb6 is None:
+        raise ValueError("temb6 is required")
+    if tuple(temb6.shape) == (T, 6, H):
+        return 6 * H
+    if tuple(temb6.shape) == (6, H):
+        return 0
+    raise ValueError("temb6 has shape %s, expected [%d, 6, %d] or [6, %d]" % (
+        list(temb6.shape), T, H, H))
+
+
+def lbv_adaln_rmsnorm(cfg, x, temb6, table, eps, h, stream=None):
+    """h = rmsnorm(x) * (1 + scale) + shift (rows 4 and 3 of table + temb6)."""
+    dt = cfg.torch_dtype
+    H = cfg.hidden
+    _shape(x, "x", None, H)
+    T = x.shape[0]
+    stride = _temb_rows(temb6, T, H)
+    _shape(table, "table", 6, H)
+    _shape(h, "h", T, H)
+    _same_device(x, temb6, table, h)
+    _check(load().lbv_adaln_rmsnorm(
+        ctypes.byref(cfg), T, _ptr(x, "x", torch.float32), _ptr(temb6, "temb6", torch.float32),
+        stride, _ptr(table, "table", torch.float32), float(eps), _ptr(h, "h", dt),
+        _stream(stream)), "lbv_adaln_rmsnorm")
+
+
+def lbv_moe_ffn_adaln_workspace_size(cfg: MoEConfig, T: int) -> int:
+    return _size("lbv_moe_ffn_adaln_workspace_size", cfg, T)
+
+
+def lbv_moe_ffn_adaln(cfg, x, mask, temb6, table, eps, router_w, e_bias, w13, w2, shared_w13,
+                      shared_w2, out, topk_ids_out, topk_w_out, ws, stream=None):
+    """The FFN half of a DiT layer: out = x + gate * block(AdaLN(x)), fp32
+    residual stream (out may be x)."""
+    dt = cfg.torch_dtype
+    H, E, K, I, ns, KS, S = _dims(cfg)
+    _shape(x, "x", None, H)
+    T = x.shape[0]
+    stride = _temb_rows(temb6, T, H)
+    _shape(table, "table", 6, H)
+    _shape(mask, "mask", T)
+    _shape(router_w, "router_w", E, H)
+    _shape(e_bias, "e_bias", E)
+    _shape(w13, "w13", E, 2 * I, H)
+    _shape(w2, "w2", E, H, I)
+    _shared_shapes(cfg, shared_w13, shared_w2)
+    _shape(out, "out", T, H)
+    _shape(topk_ids_out, "topk_ids_out", T, K)
+    _shape(topk_w_out, "topk_w_out", T, K)
+    _need(ws, "ws")
+    _same_device(x, mask, temb6, table, router_w, e_bias, w13, w2, shared_w13, shared_w2, out,
+                 topk_ids_out, topk_w_out, ws)
+    _check(load().lbv_moe_ffn_adaln(
+        ctypes.byref(cfg), T, _ptr(x, "x", torch.float32), _ptr(mask, "mask", torch.uint8),
+        _ptr(temb6, "temb6", torch.float32), stride, _ptr(table, "table", torch.float32),
+        float(eps), _ptr(router_w, "router_w", torch.float32),
+        _ptr(e_bias, "e_bias", torch.float32), _ptr(w13, "w13", dt), _ptr(w2, "w2", dt),
+        _ptr(shared_w13, "shared_w13", dt), _ptr(shared_w2, "shared_w2", dt),
+        _ptr(out, "out", torch.float32), _ptr(topk_ids_out, "topk_ids_out", torch.int32),
+        _ptr(topk_w_out, "topk_w_out", torch.float32), _ptr(ws, "ws"),
+        ws.numel() * ws.element_size(), _stream(stream)), "lbv_moe_ffn_adaln")
 
 
 class MoEBlock:

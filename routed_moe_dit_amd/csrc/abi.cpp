@@ -130,6 +130,23 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 lbv_status hip_status(hipError_t e) { return e == hipSuccess ? LBV_OK : LBV_ERR_HIP; }
 
+// The FFN half of a DiT layer: the forward workspace, then the block input h.
+size_t ffn_h_offset(const Dims& d) { return fwd_layout(d).total; }
+size_t ffn_ws_bytes(const Dims& d) {
+    return ffn_h_offset(d) + round_up(static_cast<size_t>(d.T) * d.H * elem_bytes(d));
+}
+
+// Checks of the AdaLN operands shared by lbv_adaln_rmsnorm and lbv_moe_ffn_adaln.
+lbv_status check_adaln(const Dims& d, const float* x, const float* temb6, int64_t temb_stride,
+                       const float* table, float eps) {
+    if (!x || !temb6 || !table) return LBV_ERR_NULL;
+    if (!aligned16(x) || !aligned16(temb6) || !aligned16(table)) return LBV_ERR_ALIGN;
+    if (temb_stride < 0 || temb_stride % 4 != 0) return LBV_ERR_ALIGN;
+    if (!(eps >= 0.0f) || !isfinite(eps)) return LBV_ERR_SHAPE;
+    (void)d;
+    return LBV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -289,6 +306,79 @@ lbv_status lbv_moe_gemm_w2_combine(const lbv_moe_config* cfg, int64_t T, const v
     hipError_t e = lbv::launch_gemm_w2(d, act, w2, shared_w2, offsets, sorted_rows, ws, ctr, stream);
     if (e != hipSuccess) return LBV_ERR_HIP;
     return hip_status(lbv::launch_combine(d, ws, inv_rows, topk_w, out, stream));
+}
+
+lbv_status lbv_moe_ffn_adaln_workspace_size(const lbv_moe_config* cfg, int64_t T, size_t* bytes) {
+    if (!bytes) return LBV_ERR_NULL;
+    Dims d;
+    lbv_status st = make_dims(cfg, T, &d);
+    if (st != LBV_OK) return st;
+    *bytes = ffn_ws_bytes(d);
+    return LBV_OK;
+}
+
+lbv_status lbv_adaln_rmsnorm(const lbv_moe_config* cfg, int64_t T, const float* x,
+                             const float* temb6, int64_t temb_stride, const float* table,
+                             float eps, void* h, hipStream_t stream) {
+    Dims d;
+    lbv_status st = make_dims(cfg, T, &d);
+    if (st != LBV_OK) return st;
+    if (T == 0) return LBV_OK;
+    st = check_adaln(d, x, temb6, temb_stride, table, eps);
+    if (st != LBV_OK) return st;
+    if (!h) return LBV_ERR_NULL;
+    if (!aligned16(h)) return LBV_ERR_ALIGN;
+    const size_t xb = static_cast<size_t>(T) * d.H * 4;
+    if (overlaps(x, xb, h, static_cast<size_t>(T) * d.H * elem_bytes(d))) return LBV_ERR_ALIAS;
+    lbv::AdalnArgs a{x, temb6, temb_stride, table, eps, h, T, d.H, stream};
+    return hip_status(lbv::launch_adaln(d, a));
+}
+
+lbv_status lbv_moe_ffn_adaln(const lbv_moe_config* cfg, int64_t T, const float* x,
+                             const uint8_t* mask, const float* temb6, int64_t temb_stride,
+                             const float* table, float eps, const float* router_w,
+                             const float* e_bias, const void* w13, const void* w2,
+                             const void* shared_w13, const void* shared_w2, float* out,
+                             int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+    Dims d;
+    lbv_status st = make_dims(cfg, T, &d);
+    if (st != LBV_OK) return st;
+    if (T == 0) return LBV_OK;
+    st = check_adaln(d, x, temb6, temb_stride, table, eps);
+    if (st != LBV_OK) return st;
+    if (!router_w || !e_bias || !w13 || !w2 || !out || !ws) return LBV_ERR_NULL;
+    if (d.NS > 0 && (!shared_w13 || !shared_w2)) return LBV_ERR_NULL;
+    if (!aligned16(router_w) || !aligned4(e_bias) || !aligned16(w13) || !aligned16(w2) ||
+        !aligned16(shared_w13) || !aligned16(shared_w2) || !aligned16(out) || !aligned16(ws) ||
+        !aligned4(topk_ids_out) || !aligned4(topk_w_out))
+        return LBV_ERR_ALIGN;
+    const size_t xb = static_cast<size_t>(T) * d.H * 4;
+    // in place (out == x) is allowed: each element is read, then written, by one lane
+    if (out != x && overlaps(x, xb, out, xb)) return LBV_ERR_ALIAS;
+    if (ws_bytes < ffn_ws_bytes(d)) return LBV_ERR_WORKSPACE;
+    if (overlaps(ws, ws_bytes, out, xb) || overlaps(ws, ws_bytes, x, xb)) return LBV_ERR_ALIAS;
+
+    const FwdLayout L = fwd_layout(d);
+    char* base = static_cast<char*>(ws);
+    int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(base + L.ids);
+    float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(base + L.w);
+    int32_t* offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+    int32_t* sorted = reinterpret_cast<int32_t*>(base + L.sorted);
+    int32_t* inv = reinterpret_cast<int32_t*>(base + L.inv);
+    int* ctr1 = reinterpret_cast<int*>(base + L.ctr1);
+    int* ctr2 = reinterpret_cast<int*>(base + L.ctr2);
+    void* h = base + ffn_h_offset(d);
+
+    lbv::AdalnArgs a{x, temb6, temb_stride, table, eps, h, T, d.H, stream};
+    hipError_t e = lbv::launch_adaln(d, a);
+    if (e == hipSuccess) e = lbv::launch_route(d, h, router_w, e_bias, mask, ids, w, base + L.route, stream);
+    if (e == hipSuccess) e = lbv::launch_permute(d, ids, offsets, sorted, inv, base + L.perm, stream);
+    if (e == hipSuccess) e = lbv::launch_gemm_w13(d, h, w13, shared_w13, offsets, sorted, base + L.act, ctr1, stream);
+    if (e == hipSuccess) e = lbv::launch_gemm_w2(d, base + L.act, w2, shared_w2, offsets, sorted, base + L.y, ctr2, stream);
+    if (e == hipSuccess)
+        e = lbv::launch_combine_residual(d, base + L.y, inv, w, x, temb6, temb_stride, table, out, stream);
+    return hip_status(e);
 }
 
 lbv_status lbv_moe_forward(const lbv_moe_config* cfg, int64_t T, const void* x,

@@ -868,9 +868,19 @@ struct CombArgs {
     void* out;
     int64_t T;
     int H, K, NS, KS;
+    // gated residual (RESID): out[t] = x[t] + gate[t] * sum, fp32, with
+    // gate = table[5] + temb row t [5]
+    const float* x;
+    const float* temb;
+    int64_t temb_stride;
+    const float* table;
 };
 
-template <bool BF16>
+// RESID: the sum goes, unrounded, into the gated residual of the DiT layer
+// (prhub summary of sglang PR #32341, "实现拆解" step 2: AdaLN with
+// scale_shift_table and a token-level temb6): one read of the residual row
+// and the gate, one fp32 write, instead of a round trip of the block output.
+template <bool BF16, bool RESID>
 __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -926,15 +936,33 @@ __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
                     }
                 }
             }
-            u32x4 o;
-            if (BF16) {
+            if constexpr (RESID) {
+                typedef float f32x4 __attribute__((ext_vector_type(4)));
+                const float* xr = a.x + t * a.H + h;
+                const float* g0 = a.table + 5 * a.H + h;
+                const float* g1 = a.temb + t * a.temb_stride + 5 * a.H + h;
+                float* orow = static_cast<float*>(a.out) + t * a.H + h;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+                for (int j = 0; j < EPL / 4; ++j) {
+                    const f32x4 xv = *reinterpret_cast<const f32x4*>(xr + 4 * j);
+                    const f32x4 ga = *reinterpret_cast<const f32x4*>(g0 + 4 * j);
+                    const f32x4 gb = *reinterpret_cast<const f32x4*>(g1 + 4 * j);
+                    f32x4 ov;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ov[i] = xv[i] + (ga[i] + gb[i]) * acc[4 * j + i];
+                    __builtin_nontemporal_store(ov, reinterpret_cast<f32x4*>(orow + 4 * j));
+                }
             } else {
+                u32x4 o;
+                if (BF16) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(acc[i]);
+                    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(acc[i]);
+                }
+                __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(static_cast<char*>(a.out) + (t * a.H + h) * ESZ));
             }
-            __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(static_cast<char*>(a.out) + (t * a.H + h) * ESZ));
         }
     }
 }
@@ -1039,7 +1067,7 @@ hipError_t launch_gemm_w2(const Dims& d, const void* act, const void* w2, const 
 
 hipError_t launch_combine(const Dims& d, const void* y, const int32_t* inv_rows,
                           const float* topk_w, void* out, hipStream_t stream) {
-    CombArgs a;
+    CombArgs a{};
     a.y = y;
     a.inv = inv_rows;
     a.w = topk_w;
@@ -1051,9 +1079,35 @@ hipError_t launch_combine(const Dims& d, const void* y, const int32_t* inv_rows,
     a.KS = d.KS;
     const unsigned grid = static_cast<unsigned>((d.T + 3) / 4);
     if (d.bf16)
-        hipLaunchKernelGGL(combine_kernel<true>, dim3(grid), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((combine_kernel<true, false>), dim3(grid), dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL(combine_kernel<false>, dim3(grid), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((combine_kernel<false, false>), dim3(grid), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_residual(const Dims& d, const void* y, const int32_t* inv_rows,
+                                   const float* topk_w, const float* x, const float* temb,
+                                   int64_t temb_stride, const float* table, float* out,
+                                   hipStream_t stream) {
+    CombArgs a{};
+    a.y = y;
+    a.inv = inv_rows;
+    a.w = topk_w;
+    a.out = out;
+    a.T = d.T;
+    a.H = d.H;
+    a.K = d.K;
+    a.NS = d.NS;
+    a.KS = d.KS;
+    a.x = x;
+    a.temb = temb;
+    a.temb_stride = temb_stride;
+    a.table = table;
+    const unsigned grid = static_cast<unsigned>((d.T + 3) / 4);
+    if (d.bf16)
+        hipLaunchKernelGGL((combine_kernel<true, true>), dim3(grid), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((combine_kernel<false, true>), dim3(grid), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

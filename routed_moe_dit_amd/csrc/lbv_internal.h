@@ -79,6 +79,27 @@ hipError_t launch_gemm_w2(const Dims& d, const void* act, const void* w2, const 
 hipError_t launch_combine(const Dims& d, const void* y, const int32_t* inv_rows,
                           const float* topk_w, void* out, hipStream_t stream);
 
+// AdaLN in front of the block and the gated residual after it.
+struct AdalnArgs {
+    const float* x;        // [T, H] fp32 residual stream
+    const float* temb;     // temb6 rows: token t's 6 H values at temb + t * temb_stride
+    int64_t temb_stride;   // 0: one row for every token
+    const float* table;    // scale_shift_table [6, H]
+    float eps;
+    void* h;               // [T, H] block input (cfg dtype)
+    int64_t T;
+    int H;
+    hipStream_t stream;
+};
+hipError_t launch_adaln(const Dims& d, const AdalnArgs& a);
+
+// combine + gated residual: out[t] = x[t] + gate[t] * (sum_k w y + shared y),
+// gate = table[5] + temb6 row t [5], fp32 in and out (out may be x)
+hipError_t launch_combine_residual(const Dims& d, const void* y, const int32_t* inv_rows,
+                                   const float* topk_w, const float* x, const float* temb,
+                                   int64_t temb_stride, const float* table, float* out,
+                                   hipStream_t stream);
+
 // ---------------------------------------------------------------------------
 // Device helpers
 // ---------------------------------------------------------------------------

@@ -21,7 +21,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 14, names
+    assert len(names) == 17, names
     assert set(names) == set(lbv.EXPORTS)
     L = ctypes.CDLL(lbv.LIB_PATH)
     for n in names:
@@ -320,3 +320,33 @@ def test_route_noalloc_validation_paths():
     assert r(big, 4) == lbv.LBV_ERR_SCRATCH
     # the LingBot shape fits: 1.5 MiB of planes + 2 MiB of logits
     assert lbv.lbv_moe_route_workspace_size(c) <= (8 << 20)
+
+
+def test_adaln_validation_paths():
+    """AdaLN entries reject before any launch: NULLs, misaligned rows, a
+    negative or non-finite eps, partial overlap of out and x (out == x is
+    allowed), a short workspace."""
+    c = lbv.config()
+    L = raw()
+    H = 2048
+    assert L.lbv_adaln_rmsnorm(ctypes.byref(c), 0, None, None, 0, None, 1e-6, None, None) == \
+        lbv.LBV_OK
+    assert L.lbv_adaln_rmsnorm(ctypes.byref(c), 4, A, None, 0, B, 1e-6, Cc, None) == \
+        lbv.LBV_ERR_NULL
+    assert L.lbv_adaln_rmsnorm(ctypes.byref(c), 4, A, A, 6 * H + 2, B, 1e-6, Cc, None) == \
+        lbv.LBV_ERR_ALIGN
+    assert L.lbv_adaln_rmsnorm(ctypes.byref(c), 4, A, A, 0, B, -1.0, Cc, None) == \
+        lbv.LBV_ERR_SHAPE
+    assert L.lbv_adaln_rmsnorm(ctypes.byref(c), 4, A, A, 0, B, float("nan"), Cc, None) == \
+        lbv.LBV_ERR_SHAPE
+    assert L.lbv_adaln_rmsnorm(ctypes.byref(c), 4, A, A, 0, B, 1e-6, A + 64, None) == \
+        lbv.LBV_ERR_ALIAS
+    need = lbv.lbv_moe_ffn_adaln_workspace_size(c, 16)
+    assert need == lbv.lbv_moe_workspace_size(c, 16) + 16 * H * 2
+
+    def f(out, ws_bytes=need, x=A):
+        return L.lbv_moe_ffn_adaln(ctypes.byref(c), 16, x, None, B, 0, B, 1e-6, B, B, B, B, B, B,
+                                   out, None, None, BIG, ws_bytes, None)
+    assert f(A + 4096) == lbv.LBV_ERR_ALIAS            # out overlaps x, not equal
+    assert f(Cc, ws_bytes=need - 1) == lbv.LBV_ERR_WORKSPACE
+    assert f(Cc + 8) == lbv.LBV_ERR_ALIGN
