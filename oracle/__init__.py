@@ -241,6 +241,44 @@ def ffn_adaln(wl, x, temb6, table, router_w, e_bias, w13, w2, shared_w13=None, s
     return dict(out=out, h=h, block=blk)
 
 
+def quantize_fp8_rows(w):
+    """FP8 weight rows: (codes uint8 [..., cols], power-of-two scales fp32 [...])
+    of an fp32 array whose last axis is a row."""
+    w = _f32(w)
+    rows, cols = int(np.prod(w.shape[:-1])), w.shape[-1]
+    q = np.empty(w.shape, np.uint8)
+    sc = np.empty(w.shape[:-1], np.float32)
+    L = lib()
+    L.orc_quantize_fp8_rows.argtypes = [ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 3
+    L.orc_quantize_fp8_rows.restype = None
+    L.orc_quantize_fp8_rows(rows, cols, _p(w), _p(q), _p(sc))
+    return q, sc
+
+
+def dequantize_fp8_rows(q, scale):
+    """decode(q) * scale, fp32 (exact)."""
+    q = np.ascontiguousarray(q, np.uint8)
+    scale = _f32(scale)
+    rows, cols = int(np.prod(q.shape[:-1])), q.shape[-1]
+    assert scale.shape == q.shape[:-1]
+    w = np.empty(q.shape, np.float32)
+    L = lib()
+    L.orc_dequantize_fp8_rows.argtypes = [ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 3
+    L.orc_dequantize_fp8_rows.restype = None
+    L.orc_dequantize_fp8_rows(rows, cols, _p(q), _p(scale), _p(w))
+    return w
+
+
+def e4m3_values():
+    """The value of each of the 256 e4m3fn codes (NaN for 0x7f and 0xff)."""
+    out = np.empty(256, np.float64)
+    L = lib()
+    L.orc_e4m3_decode_all.argtypes = [ctypes.c_void_p]
+    L.orc_e4m3_decode_all.restype = None
+    L.orc_e4m3_decode_all(_p(out))
+    return out
+
+
 def expert_act(wl, x_row, w13, e):
     """fp64 act [I] of routed expert e for one token."""
     x_row, w13 = _f32(x_row), _f32(w13)

@@ -488,6 +488,83 @@ void orc_bf16_round(int64_t n, const double *in, double *out)
     for (int64_t i = 0; i < n; ++i) out[i] = bf16_round_d(in[i]);
 }
 
+/* ---------------------------------------------------------------------------
+ * FP8 expert weights.  The LingBot-Video recipe of vLLM-Omni ("Known
+ * Limitations") names FP8 among the expert backends its first integration
+ * leaves out; the pages give no recipe for it.  Reading: each weight row
+ * (one output channel) is stored as OCP e4m3fn codes with one power-of-two
+ * scale 2^e, e the smallest integer with max|w| <= 448 * 2^e (e = 0 for an
+ * all-zero row), q = nearest e4m3fn value of w * 2^-e, ties to the even code.
+ * The dequantized weight is decode(q) * 2^e.
+ * ------------------------------------------------------------------------- */
+
+/* Value of an OCP e4m3fn code (bias 7, no infinities, 0x7f / 0xff NaN). */
+static double e4m3_decode(uint8_t c)
+{
+    const double s = (c & 0x80) ? -1.0 : 1.0;
+    const int e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) return s * ldexp((double)m, -9);          /* subnormal: m * 2^-9 */
+    return s * ldexp(8.0 + m, e - 10);                    /* (1 + m/8) 2^(e-7) */
+}
+
+/* Nearest e4m3fn code of a finite |v| <= 448, ties to the even code. */
+static uint8_t e4m3_encode(double v)
+{
+    const uint8_t sign = signbit(v) ? 0x80 : 0;
+    const double a = fabs(v);
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal grid of 2^-9; 8 * 2^-9 is the smallest normal, code 8 */
+        return sign | (uint8_t)rint(ldexp(a, 9));
+    }
+    int ex;
+    frexp(a, &ex);                                       /* a = f 2^ex, 0.5 <= f < 1 */
+    int E = ex - 1;                                      /* a = (1 + r/8) 2^E */
+    double r = rint(ldexp(a, 3 - E)) - 8.0;              /* mantissa steps of 2^(E-3) */
+    if (r >= 8.0) { r = 0.0; ++E; }
+    return sign | (uint8_t)(((E + 7) << 3) | (int)r);
+}
+
+/* Power-of-two exponent of a row with maximum magnitude amax. */
+static int fp8_row_exponent(double amax)
+{
+    if (amax == 0.0) return 0;
+    int x;
+    const double f = frexp(amax, &x);                    /* amax = f 2^x, 448 = 0.875 2^9 */
+    return f <= 0.875 ? x - 9 : x - 8;
+}
+
+/*
+ * Quantize rows [rows, cols] of fp32 values: q [rows, cols] codes,
+ * scale [rows] = 2^e as fp32.
+ */
+void orc_quantize_fp8_rows(int64_t rows, int64_t cols, const float *w, uint8_t *q, float *scale)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const float *wr = w + r * cols;
+        double amax = 0.0;
+        for (int64_t c = 0; c < cols; ++c) amax = fmax(amax, fabs((double)wr[c]));
+        const int e = fp8_row_exponent(amax);
+        scale[r] = (float)ldexp(1.0, e);
+        for (int64_t c = 0; c < cols; ++c) q[r * cols + c] = e4m3_encode(ldexp((double)wr[c], -e));
+    }
+}
+
+/* Dequantized rows: w[r, c] = decode(q[r, c]) * scale[r] (exact in fp32). */
+void orc_dequantize_fp8_rows(int64_t rows, int64_t cols, const uint8_t *q, const float *scale,
+                             float *w)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c)
+            w[r * cols + c] = (float)(e4m3_decode(q[r * cols + c]) * (double)scale[r]);
+}
+
+void orc_e4m3_decode_all(double *out)
+{
+    for (int c = 0; c < 256; ++c) out[c] = e4m3_decode((uint8_t)c);
+}
+
 /*
  * Token copies sorted by expert ([P2] "MoE 实现的源码级要点": tokens are
  * reordered by expert before the grouped matmuls and restored after).
