@@ -50,6 +50,9 @@ def parse():
     p.add_argument("--adaln", action="store_true",
                    help="also time the FFN half of a DiT layer around the block "
                         "(lbv_moe_ffn_adaln, token-level temb6) and its AdaLN kernel alone")
+    p.add_argument("--fp8", action="store_true",
+                   help="also time the block with fp8 (e4m3fn, per-row power-of-two scale) "
+                        "expert weights (lbv_moe_forward_fp8) and the device quantizer")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after the measurements, run a plain 1 GiB device copy three times, so "
                         "that a hardware-counter run can scale its byte counters")
@@ -319,6 +322,43 @@ def main():
             "temb6": "token-level [T, 6, H] fp32",
         }
         del temb, fws
+
+    # ---- fp8 expert weights: the same block, weights read as e4m3fn codes ----------
+    if args.fp8 and bf:
+        qev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        qev[0].record(stream)
+        wq = lbv.quantize_fp8_weights(w13, w2, sw13, sw2, stream)
+        qev[1].record(stream)
+        torch.cuda.synchronize()
+        q_ms = qev[0].elapsed_time(qev[1])
+
+        def step8():
+            lbv.lbv_moe_forward_fp8(cfg, x, mask, router_w, e_bias, wq, out, ids, wts, ws, stream)
+
+        for _ in range(args.warmup):
+            step8()
+        torch.cuda.synchronize()
+        e8 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        e8[0].record(stream)
+        for i in range(args.steps):
+            step8()
+            e8[i + 1].record(stream)
+        torch.cuda.synchronize()
+        ms8 = e8[0].elapsed_time(e8[-1]) / args.steps
+        per8 = [e8[i].elapsed_time(e8[i + 1]) for i in range(args.steps)]
+        wbytes8 = (int(hit.sum()) * 3 * I * H + 3 * I * NS * H) * (1 + 4.0 / H)
+        res["fp8"] = {
+            "ms_per_step": ms8,
+            "tokens_per_s": T / (ms8 * 1e-3),
+            "step_ms_median": pct(per8, 50),
+            "speedup_vs_bf16_weights": ms_per_step / ms8,
+            "expert_weight_bytes_read": wbytes8,
+            "expert_weight_bytes_read_bf16": weight_bytes,
+            "quantize_all_weights_ms": q_ms,
+            "format": "e4m3fn codes, one power-of-two fp32 scale per weight row; bf16 "
+                      "activations, fp32 accumulation",
+        }
+        del wq
 
     # ---- CPU oracle on a bounded sample of the same workload -----------------------
     if not args.no_cpu_baseline:

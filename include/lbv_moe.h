@@ -95,7 +95,7 @@ typedef struct {
 } lbv_moe_config;
 
 /* Version of this ABI (bumped on any signature or layout change; 2: the
- * gate/up call takes a workspace). */
+ * gate/up call takes a workspace; 3: fp8 expert weights). */
 int32_t lbv_abi_version(void);
 
 /* Human-readable name of a status code (static storage). */
@@ -247,6 +247,59 @@ lbv_status lbv_moe_forward(const lbv_moe_config *cfg, int64_t T, const void *x,
                            const void *w13, const void *w2, const void *shared_w13,
                            const void *shared_w2, void *out, int32_t *topk_ids_out,
                            float *topk_w_out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * ---------------------------------------------------------------------------
+ * FP8 expert weights.  The LingBot-Video recipe of vLLM-Omni ("Known
+ * Limitations") names FP8 among the expert backends its first integration
+ * leaves out; the pages give no recipe.  Reading taken here (weights only;
+ * activations stay bf16, accumulation fp32): row r of a weight matrix (one
+ * output channel) is stored as OCP e4m3fn codes q[r, :] (bias 7, largest
+ * finite value 448, codes 0x7f / 0xff NaN) and one scale 2^e[r], e the
+ * smallest integer with max|w[r, :]| <= 448 2^e (e = 0 for an all-zero row),
+ * q the nearest e4m3fn value of w 2^-e with ties to the even code.  The block
+ * computes exactly what the bf16 block computes with the weights
+ * decode(q) 2^e (these are exact in bf16).
+ * ---------------------------------------------------------------------------
+ */
+
+/*
+ * Quantizes `rows` rows of `cols` weights (dtype LBV_BF16 or LBV_F32, finite
+ * values) into q [rows, cols] e4m3fn codes and scale [rows] fp32 powers of
+ * two.  cols must be a positive multiple of 16; w, q 16-byte aligned, scale
+ * 4-byte aligned; q and scale must not overlap w.  rows == 0 is a no-op.
+ * Expert weights quantize as [E * 2I, H] (w13), [E * H, I] (w2),
+ * [2 I_s, H] (shared_w13) and [H, I_s] (shared_w2).
+ */
+lbv_status lbv_quantize_fp8_rows(const void *w, int32_t dtype, int64_t rows, int64_t cols,
+                                 uint8_t *q, float *scale, hipStream_t stream);
+
+/* FP8 expert weights of one layer (device pointers; the shared ones NULL iff
+ * n_shared_experts == 0; codes 16-byte, scales 4-byte aligned). */
+typedef struct {
+    const uint8_t *w13;              /* [E, 2I, H] codes                     */
+    const float *w13_scale;          /* [E, 2I]                              */
+    const uint8_t *w2;               /* [E, H, I] codes                      */
+    const float *w2_scale;           /* [E, H]                               */
+    const uint8_t *shared_w13;       /* [2 I_s, H] codes                     */
+    const float *shared_w13_scale;   /* [2 I_s]                              */
+    const uint8_t *shared_w2;        /* [H, I_s] codes                       */
+    const float *shared_w2_scale;    /* [H]; the scale of row n covers all   */
+                                     /* I_s columns (every pseudo-expert)    */
+} lbv_moe_fp8_weights;
+
+/*
+ * lbv_moe_forward with fp8 expert weights: cfg->dtype must be LBV_BF16
+ * (LBV_ERR_UNSUPPORTED otherwise); x, out bf16; router in fp32 as before;
+ * ws: lbv_moe_workspace_size bytes.  Per row the matmuls read 1 byte per
+ * weight instead of 2 and form decode(q) 2^e exactly before the bf16 matrix
+ * cores, so the result equals lbv_moe_forward's on the dequantized weights
+ * up to the order of fp32 summation.
+ */
+lbv_status lbv_moe_forward_fp8(const lbv_moe_config *cfg, int64_t T, const void *x,
+                               const uint8_t *mask, const float *router_w, const float *e_bias,
+                               const lbv_moe_fp8_weights *wq, void *out, int32_t *topk_ids_out,
+                               float *topk_w_out, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * ---------------------------------------------------------------------------

@@ -22,7 +22,9 @@ __all__ = [
     "lbv_moe_w2_workspace_size", "lbv_moe_route", "lbv_moe_route_noalloc", "lbv_moe_permute",
     "lbv_moe_gemm_w13_silu",
     "lbv_moe_gemm_w2_combine", "lbv_moe_forward", "lbv_adaln_rmsnorm",
-    "lbv_moe_ffn_adaln_workspace_size", "lbv_moe_ffn_adaln", "EXPORTS", "LIB_PATH",
+    "lbv_moe_ffn_adaln_workspace_size", "lbv_moe_ffn_adaln", "Fp8Weights",
+    "lbv_quantize_fp8_rows", "quantize_fp8_weights", "lbv_moe_forward_fp8", "EXPORTS",
+    "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblbv_moe.so")
@@ -40,6 +42,7 @@ EXPORTS = (
     "lbv_moe_w2_workspace_size", "lbv_moe_route", "lbv_moe_route_noalloc",
     "lbv_moe_permute", "lbv_moe_gemm_w13_silu", "lbv_moe_gemm_w2_combine", "lbv_moe_forward",
     "lbv_adaln_rmsnorm", "lbv_moe_ffn_adaln_workspace_size", "lbv_moe_ffn_adaln",
+    "lbv_quantize_fp8_rows", "lbv_moe_forward_fp8",
 )
 
 
@@ -74,6 +77,14 @@ def config(hidden=2048, num_experts=128, top_k=8, n_group=4, topk_group=2, inter
     return MoEConfig(hidden, num_experts, top_k, n_group, topk_group, intermediate,
                      n_shared_experts, int(bool(norm_topk_prob)), float(routed_scaling_factor),
                      sf, dt)
+
+
+class _Fp8WeightsC(ctypes.Structure):
+    """Mirror of lbv_moe_fp8_weights."""
+
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "w13", "w13_scale", "w2", "w2_scale", "shared_w13", "shared_w13_scale", "shared_w2",
+        "shared_w2_scale")]
 
 
 class LbvError(RuntimeError):
@@ -124,6 +135,11 @@ def load():
     L.lbv_moe_ffn_adaln_workspace_size.restype = st
     L.lbv_moe_ffn_adaln.argtypes = [C, I64, P, P, P, I64, P, F, P, P, P, P, P, P, P, P, P, P, SZ, P]
     L.lbv_moe_ffn_adaln.restype = st
+    L.lbv_quantize_fp8_rows.argtypes = [P, ctypes.c_int32, I64, I64, P, P, P]
+    L.lbv_quantize_fp8_rows.restype = st
+    L.lbv_moe_forward_fp8.argtypes = [C, I64, P, P, P, P, ctypes.POINTER(_Fp8WeightsC), P, P, P,
+                                      P, SZ, P]
+    L.lbv_moe_forward_fp8.restype = st
     _lib = L
     return L
 
@@ -434,6 +450,93 @@ def lbv_moe_ffn_adaln(cfg, x, mask, temb6, table, eps, router_w, e_bias, w13, w2
         _ptr(out, "out", torch.float32), _ptr(topk_ids_out, "topk_ids_out", torch.int32),
         _ptr(topk_w_out, "topk_w_out", torch.float32), _ptr(ws, "ws"),
         ws.numel() * ws.element_size(), _stream(stream)), "lbv_moe_ffn_adaln")
+
+
+def lbv_quantize_fp8_rows(w, q, scale, stream=None):
+    """q [..., cols] uint8 e4m3fn codes and scale [...] fp32 powers of two of
+    the rows of w [..., cols] (bf16 or fp32)."""
+    if w.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("w must be bfloat16 or float32, got %s" % w.dtype)
+    if w.dim() < 1:
+        raise ValueError("w must have at least one dimension")
+    _shape(q, "q", *w.shape)
+    _shape(scale, "scale", *w.shape[:-1])
+    _same_device(w, q, scale)
+    cols = w.shape[-1]
+    rows = w.numel() // cols if cols else 0
+    _check(load().lbv_quantize_fp8_rows(
+        _ptr(w, "w"), LBV_BF16 if w.dtype == torch.bfloat16 else LBV_F32, rows, cols,
+        _ptr(q, "q", torch.uint8), _ptr(scale, "scale", torch.float32), _stream(stream)),
+        "lbv_quantize_fp8_rows")
+
+
+class Fp8Weights:
+    """FP8 expert weights of one layer: codes (uint8) and row scales (fp32)
+    of w13 [E,2I,H], w2 [E,H,I], shared_w13 [2 I_s,H], shared_w2 [H,I_s]."""
+
+    def __init__(self, w13, w13_scale, w2, w2_scale, shared_w13=None, shared_w13_scale=None,
+                 shared_w2=None, shared_w2_scale=None):
+        self.w13, self.w13_scale = w13, w13_scale
+        self.w2, self.w2_scale = w2, w2_scale
+        self.shared_w13, self.shared_w13_scale = shared_w13, shared_w13_scale
+        self.shared_w2, self.shared_w2_scale = shared_w2, shared_w2_scale
+
+    def tensors(self):
+        return (self.w13, self.w13_scale, self.w2, self.w2_scale, self.shared_w13,
+                self.shared_w13_scale, self.shared_w2, self.shared_w2_scale)
+
+
+def quantize_fp8_weights(w13, w2, shared_w13=None, shared_w2=None, stream=None) -> Fp8Weights:
+    """Fp8Weights of bf16 / fp32 expert weights (device tensors), quantized on
+    the device by lbv_quantize_fp8_rows."""
+    out = []
+    for w in (w13, w2, shared_w13, shared_w2):
+        if w is None:
+            out += [None, None]
+            continue
+        q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+        sc = torch.empty(w.shape[:-1], dtype=torch.float32, device=w.device)
+        lbv_quantize_fp8_rows(w, q, sc, stream)
+        out += [q, sc]
+    return Fp8Weights(*out)
+
+
+def lbv_moe_forward_fp8(cfg, x, mask, router_w, e_bias, wq: Fp8Weights, out, topk_ids_out,
+                        topk_w_out, ws, stream=None):
+    H, E, K, I, ns, KS, S = _dims(cfg)
+    _shape(x, "x", None, H)
+    T = x.shape[0]
+    _shape(mask, "mask", T)
+    _shape(router_w, "router_w", E, H)
+    _shape(e_bias, "e_bias", E)
+    _shape(wq.w13, "w13", E, 2 * I, H)
+    _shape(wq.w13_scale, "w13_scale", E, 2 * I)
+    _shape(wq.w2, "w2", E, H, I)
+    _shape(wq.w2_scale, "w2_scale", E, H)
+    if ns > 0:
+        _shape(wq.shared_w13, "shared_w13", 2 * I * ns, H)
+        _shape(wq.shared_w13_scale, "shared_w13_scale", 2 * I * ns)
+        _shape(wq.shared_w2, "shared_w2", H, I * ns)
+        _shape(wq.shared_w2_scale, "shared_w2_scale", H)
+    elif any(t is not None for t in wq.tensors()[4:]):
+        raise ValueError("shared weights given but n_shared_experts == 0")
+    _shape(out, "out", T, H)
+    _shape(topk_ids_out, "topk_ids_out", T, K)
+    _shape(topk_w_out, "topk_w_out", T, K)
+    _need(ws, "ws")
+    _same_device(x, mask, router_w, e_bias, out, topk_ids_out, topk_w_out, ws, *wq.tensors())
+    names = ("w13", "w13_scale", "w2", "w2_scale", "shared_w13", "shared_w13_scale", "shared_w2",
+             "shared_w2_scale")
+    ptrs = [_ptr(t, n, torch.float32 if n.endswith("scale") else torch.uint8)
+            for t, n in zip(wq.tensors(), names)]
+    cw = _Fp8WeightsC(*ptrs)
+    dt = cfg.torch_dtype
+    _check(load().lbv_moe_forward_fp8(
+        ctypes.byref(cfg), T, _ptr(x, "x", dt), _ptr(mask, "mask", torch.uint8),
+        _ptr(router_w, "router_w", torch.float32), _ptr(e_bias, "e_bias", torch.float32),
+        ctypes.byref(cw), _ptr(out, "out", dt), _ptr(topk_ids_out, "topk_ids_out", torch.int32),
+        _ptr(topk_w_out, "topk_w_out", torch.float32), _ptr(ws, "ws"),
+        ws.numel() * ws.element_size(), _stream(stream)), "lbv_moe_forward_fp8")
 
 
 class MoEBlock:

@@ -13,7 +13,7 @@ using lbv::Dims;
 
 namespace {
 
-constexpr int32_t kAbiVersion = 2;
+constexpr int32_t kAbiVersion = 3;
 constexpr size_t kAlign = 256;
 
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -373,11 +373,86 @@ lbv_status lbv_moe_ffn_adaln(const lbv_moe_config* cfg, int64_t T, const float* 
     lbv::AdalnArgs a{x, temb6, temb_stride, table, eps, h, T, d.H, stream};
     hipError_t e = lbv::launch_adaln(d, a);
     if (e == hipSuccess) e = lbv::launch_route(d, h, router_w, e_bias, mask, ids, w, base + L.route, stream);
-    if (e == hipSuccess) e = lbv::launch_permute(d, ids, offsets, sorted, inv, base + L.perm, stream);
-    if (e == hipSuccess) e = lbv::launch_gemm_w13(d, h, w13, shared_w13, offsets, sorted, base + L.act, ctr1, stream);
-    if (e == hipSuccess) e = lbv::launch_gemm_w2(d, base + L.act, w2, shared_w2, offsets, sorted, base + L.y, ctr2, stream);
+    // the permutation's scan zeroes both matmuls' tile queue counters
+    if (e == hipSuccess)
+        e = lbv::launch_permute(d, ids, offsets, sorted, inv, base + L.perm, stream, ctr1, ctr2);
+    if (e == hipSuccess)
+        e = lbv::launch_gemm_w13(d, h, w13, shared_w13, offsets, sorted, base + L.act, ctr1, stream,
+                                 nullptr, nullptr, false);
+    if (e == hipSuccess)
+        e = lbv::launch_gemm_w2(d, base + L.act, w2, shared_w2, offsets, sorted, base + L.y, ctr2,
+                                stream, nullptr, nullptr, false);
     if (e == hipSuccess)
         e = lbv::launch_combine_residual(d, base + L.y, inv, w, x, temb6, temb_stride, table, out, stream);
+    return hip_status(e);
+}
+
+lbv_status lbv_quantize_fp8_rows(const void* w, int32_t dtype, int64_t rows, int64_t cols,
+                                 uint8_t* q, float* scale, hipStream_t stream) {
+    if (dtype != LBV_BF16 && dtype != LBV_F32) return LBV_ERR_UNSUPPORTED;
+    if (rows < 0 || cols <= 0 || cols % 16 != 0 || cols > (1 << 30)) return LBV_ERR_SHAPE;
+    if (rows > (int64_t(1) << 40) / cols) return LBV_ERR_SHAPE;
+    if (rows == 0) return LBV_OK;
+    if (!w || !q || !scale) return LBV_ERR_NULL;
+    if (!aligned16(w) || !aligned16(q) || !aligned4(scale)) return LBV_ERR_ALIGN;
+    const size_t n = static_cast<size_t>(rows) * static_cast<size_t>(cols);
+    const size_t wb = n * (dtype == LBV_BF16 ? 2 : 4);
+    if (overlaps(w, wb, q, n) || overlaps(w, wb, scale, static_cast<size_t>(rows) * 4) ||
+        overlaps(q, n, scale, static_cast<size_t>(rows) * 4))
+        return LBV_ERR_ALIAS;
+    return hip_status(lbv::launch_quantize_fp8(w, dtype == LBV_BF16, rows, static_cast<int>(cols),
+                                               q, scale, stream));
+}
+
+lbv_status lbv_moe_forward_fp8(const lbv_moe_config* cfg, int64_t T, const void* x,
+                               const uint8_t* mask, const float* router_w, const float* e_bias,
+                               const lbv_moe_fp8_weights* wq, void* out, int32_t* topk_ids_out,
+                               float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    Dims d;
+    lbv_status st = make_dims(cfg, T, &d);
+    if (st != LBV_OK) return st;
+    if (!d.bf16) return LBV_ERR_UNSUPPORTED;
+    if (T == 0) return LBV_OK;
+    if (!wq) return LBV_ERR_NULL;
+    if (!x || !router_w || !e_bias || !wq->w13 || !wq->w13_scale || !wq->w2 || !wq->w2_scale ||
+        !out || !ws)
+        return LBV_ERR_NULL;
+    if (d.NS > 0 && (!wq->shared_w13 || !wq->shared_w13_scale || !wq->shared_w2 ||
+                     !wq->shared_w2_scale))
+        return LBV_ERR_NULL;
+    if (!aligned16(x) || !aligned16(router_w) || !aligned4(e_bias) || !aligned16(wq->w13) ||
+        !aligned16(wq->w2) || !aligned16(wq->shared_w13) || !aligned16(wq->shared_w2) ||
+        !aligned4(wq->w13_scale) || !aligned4(wq->w2_scale) || !aligned4(wq->shared_w13_scale) ||
+        !aligned4(wq->shared_w2_scale) || !aligned16(out) || !aligned16(ws) ||
+        !aligned4(topk_ids_out) || !aligned4(topk_w_out))
+        return LBV_ERR_ALIGN;
+    const size_t xbytes = static_cast<size_t>(T) * d.H * elem_bytes(d);
+    if (overlaps(x, xbytes, out, xbytes)) return LBV_ERR_ALIAS;
+    const FwdLayout L = fwd_layout(d);
+    if (ws_bytes < L.total) return LBV_ERR_WORKSPACE;
+
+    char* base = static_cast<char*>(ws);
+    int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(base + L.ids);
+    float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(base + L.w);
+    int32_t* offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+    int32_t* sorted = reinterpret_cast<int32_t*>(base + L.sorted);
+    int32_t* inv = reinterpret_cast<int32_t*>(base + L.inv);
+    void* act = base + L.act;
+    void* y = base + L.y;
+    int* ctr1 = reinterpret_cast<int*>(base + L.ctr1);
+    int* ctr2 = reinterpret_cast<int*>(base + L.ctr2);
+
+    hipError_t e = lbv::launch_route(d, x, router_w, e_bias, mask, ids, w, base + L.route, stream);
+    // the permutation's scan zeroes both matmuls' tile queue counters
+    if (e == hipSuccess)
+        e = lbv::launch_permute(d, ids, offsets, sorted, inv, base + L.perm, stream, ctr1, ctr2);
+    if (e == hipSuccess)
+        e = lbv::launch_gemm_w13(d, x, wq->w13, wq->shared_w13, offsets, sorted, act, ctr1, stream,
+                                 wq->w13_scale, wq->shared_w13_scale, false);
+    if (e == hipSuccess)
+        e = lbv::launch_gemm_w2(d, act, wq->w2, wq->shared_w2, offsets, sorted, y, ctr2, stream,
+                                wq->w2_scale, wq->shared_w2_scale, false);
+    if (e == hipSuccess) e = lbv::launch_combine(d, y, inv, w, out, stream);
     return hip_status(e);
 }
 
@@ -415,9 +490,14 @@ lbv_status lbv_moe_forward(const lbv_moe_config* cfg, int64_t T, const void* x,
     int* ctr2 = reinterpret_cast<int*>(base + L.ctr2);
 
     hipError_t e = lbv::launch_route(d, x, router_w, e_bias, mask, ids, w, rws, stream);
-    if (e == hipSuccess) e = lbv::launch_permute(d, ids, offsets, sorted, inv, perm, stream);
-    if (e == hipSuccess) e = lbv::launch_gemm_w13(d, x, w13, shared_w13, offsets, sorted, act, ctr1, stream);
-    if (e == hipSuccess) e = lbv::launch_gemm_w2(d, act, w2, shared_w2, offsets, sorted, y, ctr2, stream);
+    // the permutation's scan zeroes both matmuls' tile queue counters
+    if (e == hipSuccess) e = lbv::launch_permute(d, ids, offsets, sorted, inv, perm, stream, ctr1, ctr2);
+    if (e == hipSuccess)
+        e = lbv::launch_gemm_w13(d, x, w13, shared_w13, offsets, sorted, act, ctr1, stream, nullptr,
+                                 nullptr, false);
+    if (e == hipSuccess)
+        e = lbv::launch_gemm_w2(d, act, w2, shared_w2, offsets, sorted, y, ctr2, stream, nullptr,
+                                nullptr, false);
     if (e == hipSuccess) e = lbv::launch_combine(d, y, inv, w, out, stream);
     return hip_status(e);
 }

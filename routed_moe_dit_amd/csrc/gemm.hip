@@ -116,6 +116,8 @@ struct GemmArgs {
     const void* A;          // gate/up: x [T, H];  down: act [rows, I]
     const void* B;          // gate/up: w13 [E, 2I, H];  down: w2 [E, H, I]
     const void* Bsh;        // gate/up: shared_w13 [2 Is, H];  down: shared_w2 [H, Is]
+    const float* Bs;        // fp8 weights: row scales of B ([E, 2I] / [E, H])
+    const float* Bshs;      // fp8 weights: row scales of Bsh ([2 Is] / [H])
     const int32_t* offsets; // [S + 1]
     const int32_t* rows;    // sorted_rows: slot id of each sorted row
     void* C;                // gate/up: act [rows, I];  down: y [rows, H]
@@ -195,7 +197,7 @@ constexpr int kMaxSeg = 512;
 // once, then runs one continuous k-loop over all its tiles: the copies of the
 // next tile's first STG-1 k-tiles are issued during the current tile's last
 // k-tiles and land while its epilogue runs.
-template <int BM, int BN, int MODE, int NW, int CWV, int ORDER, int STG>
+template <int BM, int BN, int MODE, int NW, int CWV, int ORDER, int STG, bool W8>
 __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     // NW waves: 2 along the tokens x NW/2 along the weight rows (NW = 4: one
     // wave per SIMD with 128 x 128 accumulators; NW = 8: two per SIMD with
@@ -206,13 +208,19 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     constexpr int TM = BM / 64;                  // token tiles (32 rows) per wave
     constexpr int TN = BN / WN / 32;             // weight-row tiles (32 rows) per wave
     static_assert(MODE == 1 || TN % 2 == 0, "gate/up tiles come in pairs");
-    constexpr int STAGE = (BM + BN) * BK;        // bf16 elements per stage
-    constexpr int CPR = BK / 8;                  // 16-byte chunks per row
-    constexpr int RPI = 64 / CPR;                // rows per 1 KB copy instruction
+    // B rows of a k-tile: BK bf16 (128 bytes) or, with fp8 weights (W8), BK
+    // e4m3 codes (64 bytes); lengths below are in 16-bit LDS units
+    constexpr int BKB = W8 ? BK / 2 : BK;
+    constexpr int STAGE = BM * BK + BN * BKB;    // 16-bit units per stage
+    constexpr int CPR = BK / 8;                  // 16-byte chunks per A row
+    constexpr int RPI = 64 / CPR;                // A rows per 1 KB copy instruction
+    constexpr int CPRB = BKB / 8;                // ... per B row
+    constexpr int RPIB = 64 / CPRB;              // B rows per 1 KB copy instruction
+    constexpr int EB = W8 ? 1 : 2;               // bytes per weight element in HBM
     // Waves 0 .. CW-1 issue the stage copies (with NW = 8 and CW = 4 one wave
     // per SIMD copies while the other only multiplies).
     constexpr int CW = CWV < NW ? CWV : NW;
-    constexpr int AI = BM / CW / RPI, BI = BN / CW / RPI;  // copies per copying wave per k-tile
+    constexpr int AI = BM / CW / RPI, BI = BN / CW / RPIB;  // copies per copying wave per k-tile
     constexpr int NI = AI + BI;
     constexpr int KKS = BK / 16;                 // 16-deep k-slices per k-tile
     static_assert(BM % 64 == 0 && BM <= 256 && BN == 256, "slot ids: BM/64 waves x 64 rows");
@@ -222,8 +230,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     // base register per slice plus an immediate offset for the stage and the
     // row group.  Stage STG-1 doubles as the epilogue's staging buffer.
     static_assert(STG == 2 || STG == 3, "2 or 3 stages");
-    constexpr int ASZ = BM * BK, BSZ = BN * BK;  // bf16 elements of one stage's A / B part
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[STG * STAGE];
+    constexpr int ASZ = BM * BK, BSZ = BN * BKB;  // 16-bit units of one stage's A / B part
+    // W8: the epilogue stages through a region of its own (EPW units per
+    // wave) after the stages, since a stage's B part is half as large
+    constexpr int EPW = 2048;
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[STG * STAGE + (W8 ? NW * EPW : 0)];
     __shared__ int s_pre[kMaxSeg + 1];           // m-tiles before segment s
     __shared__ int s_rid[BM];                    // slot ids of a tile's rows: gate/up: the next tile's; down: this tile's
     __shared__ int s_tmp[8];
@@ -352,7 +363,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     // A or B part; lane l lands at row +l/CPR, physical chunk l%CPR, which
     // holds logical chunk (l%CPR) ^ swz(row). ---------------------------------------
     const uint16_t* abase;
-    const uint16_t* bbase;
+    const char* bbase;                            // weight rows, bytes
     uint32_t aoff[AI], boff[BI];
     // Slot ids of a tile's BM rows, copied into s_rid by waves 0 .. BM/64-1,
     // 64 rows each (a copy like the stage copies, counted by the same waits).  The
@@ -374,14 +385,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         const int lane = (threadIdx.x & 63) + opaque_zero();
         const bool shared_seg = seg_ >= a.E;
         const int jsh = seg_ - a.E;
+        const char* B = static_cast<const char*>(a.B);
+        const char* Bsh = static_cast<const char*>(a.Bsh);
         if (MODE == 0) {
             abase = static_cast<const uint16_t*>(a.A);
-            bbase = shared_seg ? static_cast<const uint16_t*>(a.Bsh)
-                               : static_cast<const uint16_t*>(a.B) + static_cast<int64_t>(seg_) * 2 * a.I * a.H;
+            bbase = shared_seg ? Bsh : B + static_cast<int64_t>(seg_) * 2 * a.I * a.H * EB;
         } else {
             abase = static_cast<const uint16_t*>(a.A) + static_cast<int64_t>(seg_r0_) * a.I;
-            bbase = shared_seg ? static_cast<const uint16_t*>(a.Bsh) + jsh * a.I
-                               : static_cast<const uint16_t*>(a.B) + static_cast<int64_t>(seg_) * a.H * a.I;
+            bbase = shared_seg ? Bsh + jsh * a.I * EB : B + static_cast<int64_t>(seg_) * a.H * a.I * EB;
         }
 #pragma unroll
         for (int i = 0; i < AI; ++i) {
@@ -399,8 +410,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < BI; ++i) {
-            const int r = wave * (BN / CW) + i * RPI + lane / CPR;
-            const uint32_t c = (lane % CPR) ^ swz<BK>(r);
+            const int r = wave * (BN / CW) + i * RPIB + lane / CPRB;
+            const uint32_t c = (lane % CPRB) ^ swz<BKB>(r);
             if (MODE == 0) {
                 const int half = r / (BN / 2);
                 int n = nt_ * (BN / 2) + (r % (BN / 2));
@@ -411,19 +422,53 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
                 if (n >= a.I) n = a.I - 1;
                 const int row = shared_seg ? (half ? Is + jsh * a.I + n : jsh * a.I + n)
                                            : (half ? a.I + n : n);
-                boff[i] = (__umul24(row, a.H) + c * 8) * 2;
+                boff[i] = (__umul24(row, a.H) + c * (16 / EB)) * EB;
             } else {
                 int n = nt_ * BN + r;
                 n = n < lo_ ? lo_ : n;
                 n = n > hi_ ? hi_ : n;
                 if (n >= a.H) n = a.H - 1;
-                boff[i] = (__umul24(n, shared_seg ? Is : a.I) + c * 8) * 2;
+                boff[i] = (__umul24(n, shared_seg ? Is : a.I) + c * (16 / EB)) * EB;
+            }
+        }
+    };
+
+    // W8: the scale of the weight row of each of this lane's B fragments
+    // (rows clamped as in the copies), loaded for a tile ahead of its k-loop
+    constexpr int TNS = W8 ? TN : 1;
+    float sc[TNS], nsc[TNS];
+    auto load_scales = [&](int seg_, int nt_, int lo_, int hi_, float* dst) {
+        if constexpr (W8) {
+            const int ln = (threadIdx.x & 63) + opaque_zero();
+            const int rl = ln & 31;
+            const bool shared_seg = seg_ >= a.E;
+            const int jsh = seg_ - a.E;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                int idx;
+                if (MODE == 0) {
+                    constexpr int HT = TN / 2;
+                    const int half = j >= HT;
+                    int n = nt_ * (BN / 2) + wn * (BN / 2 / WN) + rl + (half ? j - HT : j) * 32;
+                    n = n < lo_ ? lo_ : n;
+                    n = n > hi_ ? hi_ : n;
+                    if (n >= a.I) n = a.I - 1;
+                    idx = shared_seg ? (half ? Is + jsh * a.I + n : jsh * a.I + n)
+                                     : seg_ * 2 * a.I + (half ? a.I + n : n);
+                } else {
+                    int n = nt_ * BN + wn * (BN / WN) + rl + j * 32;
+                    n = n < lo_ ? lo_ : n;
+                    n = n > hi_ ? hi_ : n;
+                    if (n >= a.H) n = a.H - 1;
+                    idx = shared_seg ? n : seg_ * a.H + n;
+                }
+                dst[j] = (shared_seg ? a.Bshs : a.Bs)[idx];
             }
         }
     };
 
     const int a_lds = wave * (BM / CW) * BK;     // this wave's rows inside an A / B part
-    const int b_lds = wave * (BN / CW) * BK;
+    const int b_lds = wave * (BN / CW) * BKB;
     const int nk = a.kdim / BK;
     // the k-loop of a tile runs over nkp = nk rounded up to a multiple of STG,
     // so that every step of an iteration is unconditional (no MFMA under a
@@ -449,8 +494,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         if constexpr (d < AI)
             lds_dma16_sb<d * RPI * BK * 2>(abase + kt * BK, aoff[d], lds_addr(a_part(S) + a_lds));
         else
-            lds_dma16_sb<(d - AI) * RPI * BK * 2>(bbase + kt * BK, boff[d - AI],
-                                                  lds_addr(b_part(S) + b_lds));
+            lds_dma16_sb<(d - AI) * RPIB * BKB * 2>(bbase + kt * BKB * 2, boff[d - AI],
+                                                    lds_addr(b_part(S) + b_lds));
     };
     // the same for an index d that is a constant once the loops are unrolled
     auto copy_one = [&](auto S, int kt, int d) {
@@ -462,9 +507,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     // ---- fragments: weight rows are the MFMA's first operand, token rows the
     // second, so each lane ends up with 4 consecutive output columns ----------
     // A fragment i of slice kk in stage s: fa[kk] + s*ASZ + i*32*BK; B fragment
-    // j: fb[kk] + s*BSZ + brow(j)*BK.  Formed once per tile from a lane index
+    // j: fb[kk] + s*BSZ + brow(j)*BKB.  Formed once per tile from a lane index
     // the compiler cannot see through, so that they are not held in registers
     // across the epilogue.
+    // With fp8 weights a lane's 16-byte read of a B row holds its k values of
+    // two slices: lanes 0-31 take k 0-31 of the k-tile, lanes 32-63 k 32-63,
+    // slice kk using the lane's k values 8 kk .. 8 kk + 7 of its half; the A
+    // fragments follow the same k order (chunk 4 khalf + kk).  fb[p], p = 0, 1:
+    // the B chunk of slices 2p and 2p + 1.
     const uint16_t* fa[KKS];
     const uint16_t* fb[KKS];
     auto frag_offsets = [&]() {
@@ -474,9 +524,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         const int rb = (MODE == 0 ? wn * (BN / 2 / WN) : wn * (BN / WN)) + rl;   // first B row (j = 0)
 #pragma unroll
         for (int kk = 0; kk < KKS; ++kk) {
-            const int ch = kk * 2 + kh;                          // swz(r) depends on r mod 32 only
+            const int ch = W8 ? kh * 4 + kk : kk * 2 + kh;     // swz(r) depends on r mod 32 only
             fa[kk] = lds + ra * BK + ((ch ^ swz<BK>(rl)) * 8);
-            fb[kk] = lds + STG * ASZ + rb * BK + ((ch ^ swz<BK>(rl)) * 8);
+            const int chb = W8 ? kh * 2 + (kk >> 1) : ch;
+            fb[kk] = lds + STG * ASZ + rb * BKB + ((chb ^ swz<BKB>(rl)) * 8);
         }
     };
     // B row of fragment j relative to j = 0
@@ -488,8 +539,40 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
 
     f32x16 acc[TN][TM];
     // Two fragment sets: slice g is multiplied from set g % 2 while slice g + 1
-    // is read into the other one.
+    // is read into the other one.  W8: the raw B chunks (two slices each) and
+    // the current slice's converted B fragments instead of wf0 / wf1.
     bf16x8 tf0[TM], wf0[TN], tf1[TM], wf1[TN];
+    constexpr int TNR = W8 ? TN : 1;
+    u32x4 raw[TNR];
+    bf16x8 wcv[TNR];
+    // W8: B fragments of slice ckk, decode(q) * 2^e of each lane's weight row
+    // (exact in bf16), from the low (even ckk) or high half of the raw chunk
+    auto conv = [&](int ckk) {
+        if constexpr (W8) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const uint32_t w0 = raw[j][(ckk & 1) * 2], w1 = raw[j][(ckk & 1) * 2 + 1];
+                // each conversion yields the bf16 pair of bytes (0, 1) or (2, 3)
+                // of its word as one 32-bit register; the pairs are moved as
+                // whole words (no per-element extraction)
+                const u32x4 v = {
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc[j], false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc[j], true)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc[j], false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc[j], true))};
+                wcv[j] = __builtin_bit_cast(bf16x8, v);
+            }
+        }
+    };
+    // B fragment read into set WS (bf16) or the raw chunk of an even slice (W8)
+    auto read_b = [&](bf16x8* WS, int j, int stage, int nkk) {
+        if constexpr (W8) {
+            if ((nkk & 1) == 0)
+                raw[j] = *reinterpret_cast<const u32x4*>(fb[nkk] + stage * BSZ + brow(j) * BKB);
+        } else {
+            WS[j] = *reinterpret_cast<const bf16x8*>(fb[nkk] + stage * BSZ + brow(j) * BKB);
+        }
+    };
 
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
@@ -506,6 +589,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         block_barrier();
     }
     set_sources(seg, seg_r0, seg_n, m0, nt, lo, hi);
+    load_scales(seg, nt, lo, hi, sc);
     // k-tiles 0 .. STG-2 into stages 0 .. STG-2 (zero-filled past nk)
     auto pro_fill = [&](auto S, int kt) {
         if (kt < nk) {
@@ -523,7 +607,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) tf0[i] = *reinterpret_cast<const bf16x8*>(fa[0] + i * 32 * BK);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) wf0[j] = *reinterpret_cast<const bf16x8*>(fb[0] + brow(j) * BK);
+    for (int j = 0; j < TN; ++j) read_b(wf0, j, 0, 0);
 
     constexpr int NQ = TM * TN;                  // MFMAs per slice
     constexpr int NR = TM + TN;                  // fragment reads per slice
@@ -542,10 +626,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     _Pragma("unroll") for (int q = (Q0); q < (Q1); ++q) {                                     \
         if (ZC)                                                                                \
             acc[q / TM][q % TM] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                    \
-                CW[q / TM], CT[q % TM], f32x16{}, 0, 0, 0);                                   \
+                W8 ? wcv[(q / TM) % TNR] : CW[q / TM], CT[q % TM], f32x16{}, 0, 0, 0);         \
         else                                                                                   \
             acc[q / TM][q % TM] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                    \
-                CW[q / TM], CT[q % TM], acc[q / TM][q % TM], 0, 0, 0);                        \
+                W8 ? wcv[(q / TM) % TNR] : CW[q / TM], CT[q % TM], acc[q / TM][q % TM], 0, 0, 0); \
         const int r_ = q - (Q0);                                                               \
         /* read rr goes after MFMA rr, the ones left over after the last MFMA */               \
         _Pragma("unroll") for (int rr = 0; rr < NR; ++rr) {                                   \
@@ -553,7 +637,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
                 if (rr < TM)                                                                   \
                     NT_[rr] = *reinterpret_cast<const bf16x8*>(fa[NKK] + (NB) * ASZ + rr * 32 * BK); \
                 else                                                                           \
-                    NW_[rr - TM] = *reinterpret_cast<const bf16x8*>(fb[NKK] + (NB) * BSZ + brow(rr - TM) * BK); \
+                    read_b(NW_, rr - TM, NB, NKK);                                             \
             }                                                                                  \
         }                                                                                      \
         if ((D1) > (D0)) {                                                                     \
@@ -594,6 +678,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         if (MODE == 1 && kt == 0) rid_copy(seg_r0, seg_n, m0);
 #pragma unroll
         for (int kk = 0; kk < KKS - 1; ++kk) {
+            conv(kk);
             if (kk % 2 == 0) {
                 LBV_SLICE(tf0, wf0, tf1, wf1, cur, kk + 1, 0, NQ, TS, kc, do_copy && kk < DSL,
                           kk < DSL ? kk * NI / DSL : 0, kk < DSL ? (kk + 1) * NI / DSL : 0,
@@ -605,10 +690,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
             }
         }
         // last slice (set 1)
+        conv(KKS - 1);
 #pragma unroll
         for (int q = 0; q < NPRE; ++q)
             acc[q / TM][q % TM] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                wf1[q / TM], tf1[q % TM], acc[q / TM][q % TM], 0, 0, 0);
+                W8 ? wcv[(q / TM) % TNR] : wf1[q / TM], tf1[q % TM], acc[q / TM][q % TM], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         if (kt + 1 < nkp) {
             // k-tile kt + 1 (and any slot-id copy) landed; with three stages
@@ -620,6 +706,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         block_barrier();
         if (kt == nkp - STG && has_next) {
             set_sources(nseg, nseg_r0, nseg_n, nm0, nnt, nlo, nhi);
+            load_scales(nseg, nnt, nlo, nhi, nsc);
             wait_lgkmcnt0();
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -630,16 +717,18 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     constexpr int WCOLS = MODE == 0 ? BN / 2 / WN : BN / WN;   // output columns per wave
     constexpr int CHUNKS = WCOLS / 8;                    // 16-byte chunks per row
     // staging regions in stage STG-1 (the last one a tile reads): its A and B
-    // parts split evenly when they are the same size, else all in its B part
-    constexpr bool SPLIT = ASZ == BSZ;
-    constexpr int RSZ = SPLIT ? 2 * ASZ / NW : BSZ / NW;   // staging elements per wave
+    // parts split evenly when they are the same size, else all in its B part;
+    // W8: the region after the stages
+    constexpr bool SPLIT = !W8 && ASZ == BSZ;
+    constexpr int RSZ = W8 ? EPW : SPLIT ? 2 * ASZ / NW : BSZ / NW;   // staging elements per wave
     constexpr int PT0 = RSZ / WCOLS / 32;
     constexpr int PT = PT0 < TM ? PT0 : TM;              // token tiles per staging pass
     constexpr int PROWS = PT * 32;                       // rows per staging pass
     static_assert(PT >= 1 && TM % PT == 0, "whole token tiles per pass");
     constexpr int SL = STG - 1;
-    uint16_t* const ep0 = SPLIT ? (wave < NW / 2 ? lds + SL * ASZ : lds + STG * ASZ + SL * BSZ) + (wave % (NW / 2)) * RSZ
-                                : lds + STG * ASZ + SL * BSZ + wave * RSZ;   // this wave's staging region
+    uint16_t* const ep0 = W8    ? lds + STG * STAGE + wave * RSZ
+                          : SPLIT ? (wave < NW / 2 ? lds + SL * ASZ : lds + STG * ASZ + SL * BSZ) + (wave % (NW / 2)) * RSZ
+                                  : lds + STG * ASZ + SL * BSZ + wave * RSZ;   // this wave's staging region
     auto ep_off = [&](int row, int col) {                // element offset of (row, col) in the region
         return row * WCOLS + (((col >> 3) ^ (row % CHUNKS)) << 3) + (col & 7);
     };
@@ -741,9 +830,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         set_sources(nseg, nseg_r0, nseg_n, nm0, nnt, nlo, nhi);
         frag_offsets();
 #pragma unroll
+        for (int j = 0; j < TNS; ++j) sc[j] = nsc[j];
+#pragma unroll
         for (int i = 0; i < TM; ++i) tf0[i] = *reinterpret_cast<const bf16x8*>(fa[0] + i * 32 * BK);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) wf0[j] = *reinterpret_cast<const bf16x8*>(fb[0] + brow(j) * BK);
+        for (int j = 0; j < TN; ++j) read_b(wf0, j, 0, 0);
         t = tn;
         ++it;
         seg = nseg;
@@ -1001,16 +1092,39 @@ int64_t max_mtiles(const Dims& d, int BM) {
     return (d.T * d.KS + BM - 1) / BM + d.S;
 }
 
+template <bool W8>
+void launch_w13_bf16(const Dims& d, const GemmArgs& a, hipStream_t stream) {
+    if (few_rows(d))
+        hipLaunchKernelGGL((gemm_bf16_kernel<64, G1_BN, 0, LBV_G1_WAVES, LBV_G1_COPY_WAVES, LBV_G1_ORDER, LBV_FEW_STAGES, W8>),
+                           dim3(cu_count() / 8 * 8), dim3(LBV_G1_WAVES * 64), 0, stream, a);
+    else
+        hipLaunchKernelGGL((gemm_bf16_kernel<G1_BM, G1_BN, 0, LBV_G1_WAVES, LBV_G1_COPY_WAVES, LBV_G1_ORDER, 2, W8>),
+                           dim3(cu_count() / 8 * 8), dim3(LBV_G1_WAVES * 64), 0, stream, a);
+}
+
+template <bool W8>
+void launch_w2_bf16(const Dims& d, const GemmArgs& a, hipStream_t stream) {
+    if (few_rows(d))
+        hipLaunchKernelGGL((gemm_bf16_kernel<64, G2_BN, 1, LBV_G2_WAVES, LBV_G2_COPY_WAVES, LBV_G2_ORDER, LBV_FEW_STAGES, W8>),
+                           dim3(cu_count() / 8 * 8), dim3(LBV_G2_WAVES * 64), 0, stream, a);
+    else
+        hipLaunchKernelGGL((gemm_bf16_kernel<G2_BM, G2_BN, 1, LBV_G2_WAVES, LBV_G2_COPY_WAVES, LBV_G2_ORDER, 2, W8>),
+                           dim3(cu_count() / 8 * 8), dim3(LBV_G2_WAVES * 64), 0, stream, a);
+}
+
 }  // namespace
 
 hipError_t launch_gemm_w13(const Dims& d, const void* x, const void* w13,
                            const void* shared_w13, const int32_t* offsets,
-                           const int32_t* sorted_rows, void* act, int* ctr, hipStream_t stream) {
+                           const int32_t* sorted_rows, void* act, int* ctr, hipStream_t stream,
+                           const float* w13_scale, const float* shared_w13_scale, bool zero_ctr) {
     GemmArgs a = make_args(d);
     a.ctr = ctr;
     a.A = x;
     a.B = w13;
     a.Bsh = shared_w13;
+    a.Bs = w13_scale;
+    a.Bshs = shared_w13_scale;
     a.offsets = offsets;
     a.rows = sorted_rows;
     a.C = act;
@@ -1018,13 +1132,9 @@ hipError_t launch_gemm_w13(const Dims& d, const void* x, const void* w13,
     a.ncols = d.I;
     if (d.bf16) {
         a.ntn = (d.I + G1_BN / 2 - 1) / (G1_BN / 2);
-        hipLaunchKernelGGL(zero_ctr_kernel, dim3(1), dim3(64), 0, stream, ctr);
-        if (few_rows(d))
-            hipLaunchKernelGGL((gemm_bf16_kernel<64, G1_BN, 0, LBV_G1_WAVES, LBV_G1_COPY_WAVES, LBV_G1_ORDER, LBV_FEW_STAGES>),
-                               dim3(cu_count() / 8 * 8), dim3(LBV_G1_WAVES * 64), 0, stream, a);
-        else
-            hipLaunchKernelGGL((gemm_bf16_kernel<G1_BM, G1_BN, 0, LBV_G1_WAVES, LBV_G1_COPY_WAVES, LBV_G1_ORDER, 2>),
-                               dim3(cu_count() / 8 * 8), dim3(LBV_G1_WAVES * 64), 0, stream, a);
+        if (zero_ctr) hipLaunchKernelGGL(zero_ctr_kernel, dim3(1), dim3(64), 0, stream, ctr);
+        if (w13_scale) launch_w13_bf16<true>(d, a, stream);
+        else launch_w13_bf16<false>(d, a, stream);
     } else {
         a.ntn = (d.I + 31) / 32;
         const int64_t grid = max_mtiles(d, 32) * a.ntn;
@@ -1036,12 +1146,15 @@ hipError_t launch_gemm_w13(const Dims& d, const void* x, const void* w13,
 
 hipError_t launch_gemm_w2(const Dims& d, const void* act, const void* w2, const void* shared_w2,
                           const int32_t* offsets, const int32_t* sorted_rows, void* y, int* ctr,
-                          hipStream_t stream) {
+                          hipStream_t stream, const float* w2_scale, const float* shared_w2_scale,
+                          bool zero_ctr) {
     GemmArgs a = make_args(d);
     a.ctr = ctr;
     a.A = act;
     a.B = w2;
     a.Bsh = shared_w2;
+    a.Bs = w2_scale;
+    a.Bshs = shared_w2_scale;
     a.offsets = offsets;
     a.rows = sorted_rows;                        // slot of each sorted row: y is stored in slot order
     a.C = y;
@@ -1049,13 +1162,9 @@ hipError_t launch_gemm_w2(const Dims& d, const void* act, const void* w2, const 
     a.ncols = d.H;
     if (d.bf16) {
         a.ntn = (d.H + G2_BN - 1) / G2_BN;
-        hipLaunchKernelGGL(zero_ctr_kernel, dim3(1), dim3(64), 0, stream, ctr);
-        if (few_rows(d))
-            hipLaunchKernelGGL((gemm_bf16_kernel<64, G2_BN, 1, LBV_G2_WAVES, LBV_G2_COPY_WAVES, LBV_G2_ORDER, LBV_FEW_STAGES>),
-                               dim3(cu_count() / 8 * 8), dim3(LBV_G2_WAVES * 64), 0, stream, a);
-        else
-            hipLaunchKernelGGL((gemm_bf16_kernel<G2_BM, G2_BN, 1, LBV_G2_WAVES, LBV_G2_COPY_WAVES, LBV_G2_ORDER, 2>),
-                               dim3(cu_count() / 8 * 8), dim3(LBV_G2_WAVES * 64), 0, stream, a);
+        if (zero_ctr) hipLaunchKernelGGL(zero_ctr_kernel, dim3(1), dim3(64), 0, stream, ctr);
+        if (w2_scale) launch_w2_bf16<true>(d, a, stream);
+        else launch_w2_bf16<false>(d, a, stream);
     } else {
         a.ntn = (d.H + 31) / 32;
         const int64_t grid = max_mtiles(d, 32) * a.ntn;

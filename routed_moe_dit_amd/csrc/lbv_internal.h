@@ -59,22 +59,36 @@ constexpr size_t kRouteScratchBytes = size_t(8) << 20;
 constexpr int kMaxDevices = 64;
 hipError_t route_scratch(void** ptr);
 
+// zero_ctr0 / zero_ctr1: optional tile queue counters (8 ints each) of the
+// matmuls that follow on the stream, zeroed by the permutation's scan, so that
+// those matmuls can be launched with zero_ctr = false.
 size_t permute_ws_bytes(const Dims& d);
 hipError_t launch_permute(const Dims& d, const int32_t* topk_ids, int32_t* offsets,
                           int32_t* sorted_rows, int32_t* inv_rows, void* ws,
-                          hipStream_t stream);
+                          hipStream_t stream, int* zero_ctr0 = nullptr,
+                          int* zero_ctr1 = nullptr);
 
 // The grouped matmuls take `ctr`: 8 ints of device scratch for their tile
-// queues (zeroed on the stream by the launcher).
+// queues, zero when the matmul starts: the launcher zeroes them on the stream
+// unless zero_ctr is false (the caller has zeroed them earlier on the same
+// stream, e.g. in the permutation).  With row scales (bf16 activations only)
+// the weights are e4m3fn codes, one power-of-two scale per weight row.
 constexpr size_t kGemmCtrBytes = 256;
 
 hipError_t launch_gemm_w13(const Dims& d, const void* x, const void* w13,
                            const void* shared_w13, const int32_t* offsets,
-                           const int32_t* sorted_rows, void* act, int* ctr, hipStream_t stream);
+                           const int32_t* sorted_rows, void* act, int* ctr, hipStream_t stream,
+                           const float* w13_scale = nullptr,
+                           const float* shared_w13_scale = nullptr, bool zero_ctr = true);
 
 hipError_t launch_gemm_w2(const Dims& d, const void* act, const void* w2, const void* shared_w2,
                           const int32_t* offsets, const int32_t* sorted_rows, void* y, int* ctr,
-                          hipStream_t stream);
+                          hipStream_t stream, const float* w2_scale = nullptr,
+                          const float* shared_w2_scale = nullptr, bool zero_ctr = true);
+
+// e4m3fn codes and power-of-two scales of weight rows (bf16 or fp32 source)
+hipError_t launch_quantize_fp8(const void* w, int src_bf16, int64_t rows, int cols, uint8_t* q,
+                               float* scale, hipStream_t stream);
 
 hipError_t launch_combine(const Dims& d, const void* y, const int32_t* inv_rows,
                           const float* topk_w, void* out, hipStream_t stream);

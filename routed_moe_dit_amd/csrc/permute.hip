@@ -33,6 +33,8 @@ struct PermArgs {
     int32_t* offsets;      // [S+1]
     int32_t* sorted_rows;
     int32_t* inv_rows;
+    int* ctr0;             // optional: tile queue counters of the matmuls that
+    int* ctr1;             // follow on the stream, zeroed by the scan (8 ints each)
     int64_t T;
     int K, E, NS, KS, nb;
 };
@@ -102,6 +104,10 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp /*[4]*/, int
 __global__ __launch_bounds__(PB) void perm_scan_kernel(PermArgs a) {
     __shared__ int tmp[4];
     const int tid = threadIdx.x;
+    if (tid < 8) {
+        if (a.ctr0) a.ctr0[tid] = 0;
+        if (a.ctr1) a.ctr1[tid] = 0;
+    }
     // per expert: block offsets (in place) and the expert's total
     // (chunks of 16 independent loads, so that the column is not walked one
     // memory latency per block)
@@ -181,8 +187,10 @@ size_t permute_ws_bytes(const Dims& d) {
 
 hipError_t launch_permute(const Dims& d, const int32_t* topk_ids, int32_t* offsets,
                           int32_t* sorted_rows, int32_t* inv_rows, void* ws,
-                          hipStream_t stream) {
+                          hipStream_t stream, int* zero_ctr0, int* zero_ctr1) {
     PermArgs a;
+    a.ctr0 = zero_ctr0;
+    a.ctr1 = zero_ctr1;
     a.ids = topk_ids;
     a.blk = static_cast<int32_t*>(ws);
     a.offsets = offsets;

@@ -21,7 +21,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 17, names
+    assert len(names) == 19, names
     assert set(names) == set(lbv.EXPORTS)
     L = ctypes.CDLL(lbv.LIB_PATH)
     for n in names:
@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert lbv.lbv_abi_version() == 2
+    assert lbv.lbv_abi_version() == 3
     texts = {lbv.lbv_status_string(s) for s in range(9)}
     assert len(texts) == 9
     assert lbv.lbv_status_string(99) == "unknown status"
@@ -350,3 +350,53 @@ def test_adaln_validation_paths():
     assert f(A + 4096) == lbv.LBV_ERR_ALIAS            # out overlaps x, not equal
     assert f(Cc, ws_bytes=need - 1) == lbv.LBV_ERR_WORKSPACE
     assert f(Cc + 8) == lbv.LBV_ERR_ALIGN
+
+
+def test_fp8_validation_paths():
+    """The fp8 entries reject before any launch: dtype, shapes, NULLs,
+    alignment, overlap, the fp32 config, a short workspace."""
+    L = raw()
+    q = L.lbv_quantize_fp8_rows
+    assert q(A, 2, 4, 64, B, Cc, None) == lbv.LBV_ERR_UNSUPPORTED        # dtype
+    assert q(A, lbv.LBV_BF16, 4, 24, B, Cc, None) == lbv.LBV_ERR_SHAPE    # cols % 16
+    assert q(A, lbv.LBV_BF16, 4, 0, B, Cc, None) == lbv.LBV_ERR_SHAPE
+    assert q(A, lbv.LBV_BF16, -1, 64, B, Cc, None) == lbv.LBV_ERR_SHAPE
+    assert q(None, lbv.LBV_BF16, 0, 64, None, None, None) == lbv.LBV_OK   # no rows
+    assert q(A, lbv.LBV_BF16, 4, 64, None, Cc, None) == lbv.LBV_ERR_NULL
+    assert q(A, lbv.LBV_BF16, 4, 64, B + 8, Cc, None) == lbv.LBV_ERR_ALIGN
+    assert q(A, lbv.LBV_BF16, 4, 64, B, Cc + 2, None) == lbv.LBV_ERR_ALIGN
+    assert q(A, lbv.LBV_F32, 4, 64, A + 512, Cc, None) == lbv.LBV_ERR_ALIAS   # q inside w
+    assert q(A, lbv.LBV_F32, 4, 64, B, B + 128, None) == lbv.LBV_ERR_ALIAS    # scale inside q
+
+    c = lbv.config()
+    W = lbv._Fp8WeightsC(A, B, A, B, A, B, A, B)
+    need = lbv.lbv_moe_workspace_size(c, 16)
+
+    def f(T, out=Cc, ws=BIG, ws_bytes=need, cfg=c, w=W):
+        return L.lbv_moe_forward_fp8(ctypes.byref(cfg), T, A, None, A, B,
+                                     ctypes.byref(w) if w is not None else None, out, None, None,
+                                     ws, ws_bytes, None)
+    assert f(16, cfg=lbv.config(dtype="f32")) == lbv.LBV_ERR_UNSUPPORTED
+    assert f(0) == lbv.LBV_OK
+    assert f(16, w=None) == lbv.LBV_ERR_NULL
+    assert f(16, w=lbv._Fp8WeightsC(A, B, A, None, A, B, A, B)) == lbv.LBV_ERR_NULL
+    assert f(16, w=lbv._Fp8WeightsC(A, B, A, B, None, B, A, B)) == lbv.LBV_ERR_NULL  # shared expert
+    assert f(16, w=lbv._Fp8WeightsC(A + 8, B, A, B, A, B, A, B)) == lbv.LBV_ERR_ALIGN
+    assert f(16, w=lbv._Fp8WeightsC(A, B + 2, A, B, A, B, A, B)) == lbv.LBV_ERR_ALIGN
+    assert f(16, out=A) == lbv.LBV_ERR_ALIAS
+    assert f(16, ws_bytes=need - 1) == lbv.LBV_ERR_WORKSPACE
+    c0 = lbv.config(n_shared_experts=0)
+    assert f(0, cfg=c0, w=lbv._Fp8WeightsC(A, B, A, B, None, None, None, None)) == lbv.LBV_OK
+
+
+def test_fp8_binding_shape_checks():
+    import torch
+    w = torch.zeros(4, 64)
+    with pytest.raises(ValueError, match="q has shape"):
+        lbv.lbv_quantize_fp8_rows(w, torch.zeros(4, 32, dtype=torch.uint8), torch.zeros(4))
+    with pytest.raises(ValueError, match="scale has shape"):
+        lbv.lbv_quantize_fp8_rows(w, torch.zeros(4, 64, dtype=torch.uint8), torch.zeros(5))
+    with pytest.raises(ValueError, match="bfloat16 or float32"):
+        lbv.lbv_quantize_fp8_rows(w.half(), torch.zeros(4, 64, dtype=torch.uint8), torch.zeros(4))
+    with pytest.raises(ValueError, match="device tensor"):
+        lbv.lbv_quantize_fp8_rows(w, torch.zeros(4, 64, dtype=torch.uint8), torch.zeros(4))
