@@ -279,6 +279,93 @@ def e4m3_values():
     return out
 
 
+def linear(x, w, b=None):
+    """x [T, C] @ w[N, C]^T (+ b[N]) in fp64 (plain loops in C)."""
+    x, w, b = _f32(x), _f32(w), _f32(b)
+    T, C = x.shape
+    N = w.shape[0]
+    assert w.shape == (N, C) and (b is None or b.shape == (N,))
+    y = np.empty((T, N), np.float64)
+    L = lib()
+    L.orc_linear.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 4
+    L.orc_linear.restype = None
+    L.orc_linear(T, N, C, _p(x), _p(w), _p(b), _p(y))
+    return y
+
+
+def head_rmsnorm(u, g, eps):
+    """u / sqrt(mean(u^2) + eps) * g over the last axis (length D), fp64."""
+    u = np.ascontiguousarray(u, np.float64)
+    g = _f32(g)
+    D = u.shape[-1]
+    assert g.shape == (D,)
+    y = np.empty_like(u)
+    L = lib()
+    L.orc_head_rmsnorm.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_double, ctypes.c_void_p]
+    L.orc_head_rmsnorm.restype = None
+    L.orc_head_rmsnorm(u.size // D, D, _p(u), _p(g), float(eps), _p(y))
+    return y
+
+
+def rope(u, cos, sin):
+    """Rotary embedding with neox style off on u [T, heads, D]; cos, sin [T, D/2]."""
+    u = np.ascontiguousarray(u, np.float64)
+    cos, sin = _f32(cos), _f32(sin)
+    T, heads, D = u.shape
+    assert cos.shape == (T, D // 2) and sin.shape == (T, D // 2)
+    y = np.empty_like(u)
+    L = lib()
+    L.orc_rope.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 4
+    L.orc_rope.restype = None
+    L.orc_rope(T, heads, D, _p(u), _p(cos), _p(sin), _p(y))
+    return y
+
+
+def attention(q, k, v, S, mask=None, qrows=None):
+    """Masked, per-sample softmax attention (fp64) of q, k, v [T, heads, D]
+    (fp32 values); samples are consecutive runs of S tokens.  Returns
+    o [len(qrows) or T, heads, D]."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    T, heads, D = q.shape
+    assert k.shape == q.shape and v.shape == q.shape
+    m = None if mask is None else np.ascontiguousarray(mask, np.uint8)
+    assert m is None or m.shape == (T,)
+    rows = None if qrows is None else np.ascontiguousarray(qrows, np.int64)
+    nq = T if rows is None else len(rows)
+    o = np.empty((nq, heads, D), np.float64)
+    L = lib()
+    L.orc_attention.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int] + \
+        [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    L.orc_attention.restype = None
+    L.orc_attention(T, int(S), heads, D, _p(q), _p(k), _p(v), _p(m), nq, _p(rows), _p(o))
+    return o
+
+
+def attn_qkv(x, w_qkv, b_qkv, g_q, g_k, eps, cos, sin, heads):
+    """q, k, v [T, heads, D] as a bf16 model forms them: the fused projection
+    rounded to bf16, the q / k head norms rounded to bf16, the rotary
+    embedding rounded to bf16 (fp32 values, bf16-exact)."""
+    T, H = x.shape
+    D = H // heads
+    qkv = bf16_round(linear(x, w_qkv, b_qkv)).reshape(T, 3, heads, D)
+    qn = bf16_round(head_rmsnorm(qkv[:, 0], g_q, eps))
+    kn = bf16_round(head_rmsnorm(qkv[:, 1], g_k, eps))
+    q = bf16_round(rope(qn, cos, sin)).astype(np.float32)
+    k = bf16_round(rope(kn, cos, sin)).astype(np.float32)
+    return q, k, qkv[:, 2].astype(np.float32)
+
+
+def attn_forward(x, w_qkv, b_qkv, g_q, g_k, eps, cos, sin, heads, S, mask, w_o, b_o, qrows=None):
+    """The attention half's block output [len(qrows) or T, H] (fp32 values of
+    bf16): projections, head norms, rotary embedding, attention, output
+    projection, each rounded to bf16 like the module it stands for."""
+    T, H = x.shape
+    q, k, v = attn_qkv(x, w_qkv, b_qkv, g_q, g_k, eps, cos, sin, heads)
+    o = bf16_round(attention(q, k, v, S, mask, qrows)).reshape(-1, H).astype(np.float32)
+    return bf16_round(linear(o, w_o, b_o)).astype(np.float32)
+
+
 def expert_act(wl, x_row, w13, e):
     """fp64 act [I] of routed expert e for one token."""
     x_row, w13 = _f32(x_row), _f32(w13)

@@ -565,6 +565,123 @@ void orc_e4m3_decode_all(double *out)
     for (int c = 0; c < 256; ++c) out[c] = e4m3_decode((uint8_t)c);
 }
 
+/* ---------------------------------------------------------------------------
+ * The attention half of a LingBot-Video DiT layer (prhub summary of sglang PR
+ * #32341, the LingBotVideoAttention excerpt under "关键源码片段" and "实现拆解"
+ * step 2): q, k, v are linear projections of the layer input; q and k get an
+ * RMSNorm over each head's D channels (fp32 module, learnable weight of D),
+ * then the rotary embedding with neox style off (channels 2i and 2i + 1 form
+ * a pair turned by the angle whose cos / sin the caller's tables hold for
+ * that token and i); attention is non-causal with the default scale
+ * 1 / sqrt(D), over the video;text tokens of the token's own sample, padding
+ * keys excluded; the heads' outputs go through the output projection.
+ * Readings (the pages give no formula): y = x W^T + b for the projections;
+ * rmsnorm(u) = u / sqrt(mean(u^2) + eps) * g; a padding query's output is 0.
+ * Everything here is fp64; the roundings to bf16 between the steps are the
+ * caller's (oracle/__init__.py), at the module boundaries of a bf16 model.
+ * ------------------------------------------------------------------------- */
+
+/* y[t, n] = sum_c x[t, c] w[n, c] (+ b[n]): x [T, C], w [N, C], y [T, N]. */
+void orc_linear(int64_t T, int N, int C, const float *x, const float *w, const float *b,
+                double *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const float *xr = x + t * C;
+        for (int n = 0; n < N; ++n) {
+            const float *wr = w + (int64_t)n * C;
+            double acc = 0.0;
+            for (int c = 0; c < C; ++c) acc += (double)xr[c] * (double)wr[c];
+            y[t * N + n] = acc + (b ? (double)b[n] : 0.0);
+        }
+    }
+}
+
+/* RMSNorm of every row of D values: y = u / sqrt(mean(u^2) + eps) * g. */
+void orc_head_rmsnorm(int64_t rows, int D, const double *u, const float *g, double eps, double *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const double *ur = u + r * D;
+        double ss = 0.0;
+        for (int i = 0; i < D; ++i) ss += ur[i] * ur[i];
+        const double inv = 1.0 / sqrt(ss / D + eps);
+        for (int i = 0; i < D; ++i) y[r * D + i] = ur[i] * inv * (double)g[i];
+    }
+}
+
+/*
+ * Rotary embedding, neox style off: for token t, head h and pair i < D/2,
+ *   y[2i]   = u[2i] cos(t, i) - u[2i+1] sin(t, i)
+ *   y[2i+1] = u[2i+1] cos(t, i) + u[2i] sin(t, i)
+ * u, y [T, heads, D]; cs, sn [T, D/2].
+ */
+void orc_rope(int64_t T, int heads, int D, const double *u, const float *cs, const float *sn,
+              double *y)
+{
+    const int P = D / 2;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int h = 0; h < heads; ++h)
+            for (int i = 0; i < P; ++i) {
+                const double c = cs[t * P + i], s = sn[t * P + i];
+                const double *ur = u + (t * heads + h) * D;
+                double *yr = y + (t * heads + h) * D;
+                yr[2 * i] = ur[2 * i] * c - ur[2 * i + 1] * s;
+                yr[2 * i + 1] = ur[2 * i + 1] * c + ur[2 * i] * s;
+            }
+}
+
+/*
+ * Attention of the query rows qrows[0..nq) (all T rows when qrows is NULL):
+ * token t belongs to sample t / S; its keys are the tokens of that sample
+ * with mask 1 (every token when mask is NULL).  o[r, h] = sum_j p_j v[j, h],
+ * p = softmax_j(q[t, h] . k[j, h] / sqrt(D)); 0 for a padding query or a
+ * sample without keys.  q, k, v [T, heads, D]; o [nq, heads, D].
+ */
+void orc_attention(int64_t T, int64_t S, int heads, int D, const float *q, const float *k,
+                   const float *v, const uint8_t *mask, int64_t nq, const int64_t *qrows,
+                   double *o)
+{
+    const double scale = 1.0 / sqrt((double)D);
+#pragma omp parallel
+    {
+        double *sc = malloc(sizeof(double) * (size_t)S);
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < nq; ++r) {
+            const int64_t t = qrows ? qrows[r] : r;
+            const int64_t j0 = t / S * S, j1 = j0 + S < T ? j0 + S : T;
+            for (int h = 0; h < heads; ++h) {
+                double *orow = o + (r * heads + h) * D;
+                for (int i = 0; i < D; ++i) orow[i] = 0.0;
+                if (mask && !mask[t]) continue;
+                const float *qr = q + (t * heads + h) * D;
+                double mx = -INFINITY;
+                for (int64_t j = j0; j < j1; ++j) {
+                    sc[j - j0] = -INFINITY;
+                    if (mask && !mask[j]) continue;
+                    const float *kr = k + (j * heads + h) * D;
+                    double d = 0.0;
+                    for (int i = 0; i < D; ++i) d += (double)qr[i] * (double)kr[i];
+                    sc[j - j0] = d * scale;
+                    if (sc[j - j0] > mx) mx = sc[j - j0];
+                }
+                if (mx == -INFINITY) continue;              /* no keys */
+                double den = 0.0;
+                for (int64_t j = j0; j < j1; ++j) {
+                    if (sc[j - j0] == -INFINITY) continue;
+                    const double p = exp(sc[j - j0] - mx);
+                    den += p;
+                    const float *vr = v + (j * heads + h) * D;
+                    for (int i = 0; i < D; ++i) orow[i] += p * (double)vr[i];
+                }
+                for (int i = 0; i < D; ++i) orow[i] /= den;
+            }
+        }
+        free(sc);
+    }
+}
+
 /*
  * Token copies sorted by expert ([P2] "MoE 实现的源码级要点": tokens are
  * reordered by expert before the grouped matmuls and restored after).
