@@ -95,7 +95,8 @@ typedef struct {
 } lbv_moe_config;
 
 /* Version of this ABI (bumped on any signature or layout change; 2: the
- * gate/up call takes a workspace; 3: fp8 expert weights). */
+ * gate/up call takes a workspace; 3: fp8 expert weights; 4: the attention
+ * half). */
 int32_t lbv_abi_version(void);
 
 /* Human-readable name of a status code (static storage). */
@@ -347,6 +348,82 @@ lbv_status lbv_moe_ffn_adaln(const lbv_moe_config *cfg, int64_t T, const float *
                              const void *shared_w13, const void *shared_w2, float *out,
                              int32_t *topk_ids_out, float *topk_w_out, void *ws, size_t ws_bytes,
                              hipStream_t stream);
+
+/*
+ * ---------------------------------------------------------------------------
+ * The attention half of a DiT layer (prhub summary of sglang PR #32341, the
+ * LingBotVideoAttention excerpt under "关键源码片段" and "实现拆解" step 2):
+ * joint self-attention over each sample's video;text tokens.  Per layer:
+ *   qkv = x [W_q; W_k; W_v]^T + b_qkv    (one fused projection, bf16 out)
+ *   q, k: RMSNorm over each head's D = 128 channels with weights g_q, g_k
+ *         (fp32, rounded to bf16), then the rotary embedding with neox style
+ *         off: channels (2i, 2i+1) of token t turned by cos / sin [t, i]
+ *         (fp32 tables, D/2 per token; rounded to bf16)
+ *   o = softmax(q k^T / sqrt(D)) v per head, over the valid tokens of the
+ *       query's own sample (samples are runs of S tokens; a padding query
+ *       gives 0)
+ *   out = o W_o^T + b_o                  (bf16)
+ * Readings taken where the pages are silent: head_dim is 128 (hidden /
+ * num_heads must be 128); rmsnorm(u) = u / sqrt(mean(u^2) + eps) * g; the
+ * projections carry a bias (NULL for none); the roundings sit at the module
+ * boundaries of a bf16 model.  Tokens are B samples of S rows each (padding
+ * rows inside a sample marked 0 in mask), S <= 65536.
+ * ---------------------------------------------------------------------------
+ */
+typedef struct {
+    int32_t hidden;                  /* H = num_heads * 128                 */
+    int32_t num_heads;
+    float eps;                       /* of the q / k head norms             */
+} lbv_attn_config;
+
+/* Workspace of lbv_attn_forward for B samples of S tokens: 512 bytes plus
+ * qkv [T, 3H], q, k, o [T, H] and vt [B, heads, 128, Sp] in bf16 (T = B S,
+ * Sp = S rounded up to 64). */
+lbv_status lbv_attn_workspace_size(const lbv_attn_config *cfg, int64_t B, int64_t S,
+                                   size_t *bytes);
+
+/*
+ * Dense projection y [T, N] = x [T, K] w[N, K]^T (+ bias [N], fp32, or NULL),
+ * bf16 in and out, fp32 accumulation, one rounding; on the grouped matmul
+ * kernel with a single segment.  N, K multiples of 64; T < 2^24; x and w each
+ * under 4 GiB.  ws: 512 bytes of device scratch (set on the stream).
+ */
+lbv_status lbv_linear_bf16(int64_t T, int32_t N, int32_t K, const void *x, const void *w,
+                           const float *bias, void *y, void *ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/*
+ * q / k head norms and rotary embedding, and v transposed for the attention
+ * kernel: from qkv [B S, 3H] (bf16) write q, k [B S, H] (bf16) and
+ * vt [B, heads, 128, Sp] (bf16, key positions contiguous per channel; inside
+ * every 16 keys the positions of keys 4-7 and 8-11 are swapped; zeros past S).
+ * g_q, g_k [128] fp32; cos, sin [B S, 64] fp32.
+ */
+lbv_status lbv_attn_qk_prep(const lbv_attn_config *cfg, int64_t B, int64_t S, const void *qkv,
+                            const float *g_q, const float *g_k, const float *cos_t,
+                            const float *sin_t, void *q, void *k, void *vt, hipStream_t stream);
+
+/*
+ * Masked per-sample attention o [B S, H] (bf16) from q, k [B S, H] and vt as
+ * lbv_attn_qk_prep writes them; mask u8 [B S] or NULL (every token valid).
+ */
+lbv_status lbv_attn_core(const lbv_attn_config *cfg, int64_t B, int64_t S, const void *q,
+                         const void *k, const void *vt, const uint8_t *mask, void *o,
+                         hipStream_t stream);
+
+/*
+ * The whole attention half: projection, prep, attention, output projection.
+ *   x [B S, H] bf16 (the modulated layer input); mask u8 [B S] or NULL;
+ *   w_qkv [3H, H] bf16 (rows of W_q, W_k, W_v); b_qkv [3H] fp32 or NULL;
+ *   g_q, g_k [128] fp32; cos_t, sin_t [B S, 64] fp32; w_o [H, H] bf16;
+ *   b_o [H] fp32 or NULL; out [B S, H] bf16 (must not overlap x or ws);
+ *   ws: lbv_attn_workspace_size bytes.
+ */
+lbv_status lbv_attn_forward(const lbv_attn_config *cfg, int64_t B, int64_t S, const void *x,
+                            const uint8_t *mask, const void *w_qkv, const float *b_qkv,
+                            const float *g_q, const float *g_k, const float *cos_t,
+                            const float *sin_t, const void *w_o, const float *b_o, void *out,
+                            void *ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

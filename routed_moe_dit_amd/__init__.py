@@ -23,8 +23,9 @@ __all__ = [
     "lbv_moe_gemm_w13_silu",
     "lbv_moe_gemm_w2_combine", "lbv_moe_forward", "lbv_adaln_rmsnorm",
     "lbv_moe_ffn_adaln_workspace_size", "lbv_moe_ffn_adaln", "Fp8Weights",
-    "lbv_quantize_fp8_rows", "quantize_fp8_weights", "lbv_moe_forward_fp8", "EXPORTS",
-    "LIB_PATH",
+    "lbv_quantize_fp8_rows", "quantize_fp8_weights", "lbv_moe_forward_fp8", "AttnConfig",
+    "attn_config", "attn_sp", "lbv_attn_workspace_size", "lbv_linear_bf16", "lbv_attn_qk_prep",
+    "lbv_attn_core", "lbv_attn_forward", "EXPORTS", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblbv_moe.so")
@@ -42,7 +43,8 @@ EXPORTS = (
     "lbv_moe_w2_workspace_size", "lbv_moe_route", "lbv_moe_route_noalloc",
     "lbv_moe_permute", "lbv_moe_gemm_w13_silu", "lbv_moe_gemm_w2_combine", "lbv_moe_forward",
     "lbv_adaln_rmsnorm", "lbv_moe_ffn_adaln_workspace_size", "lbv_moe_ffn_adaln",
-    "lbv_quantize_fp8_rows", "lbv_moe_forward_fp8",
+    "lbv_quantize_fp8_rows", "lbv_moe_forward_fp8", "lbv_attn_workspace_size", "lbv_linear_bf16",
+    "lbv_attn_qk_prep", "lbv_attn_core", "lbv_attn_forward",
 )
 
 
@@ -77,6 +79,25 @@ def config(hidden=2048, num_experts=128, top_k=8, n_group=4, topk_group=2, inter
     return MoEConfig(hidden, num_experts, top_k, n_group, topk_group, intermediate,
                      n_shared_experts, int(bool(norm_topk_prob)), float(routed_scaling_factor),
                      sf, dt)
+
+
+class AttnConfig(ctypes.Structure):
+    """Mirror of lbv_attn_config."""
+
+    _fields_ = [("hidden", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("eps", ctypes.c_float)]
+
+    @property
+    def head_dim(self):
+        return self.hidden // self.num_heads
+
+
+def attn_config(hidden=2048, num_heads=16, eps=1e-6) -> AttnConfig:
+    return AttnConfig(hidden, num_heads, float(eps))
+
+
+def attn_sp(S: int) -> int:
+    """Key positions per channel row of vt: S rounded up to 64."""
+    return (S + 63) // 64 * 64
 
 
 class _Fp8WeightsC(ctypes.Structure):
@@ -140,6 +161,17 @@ def load():
     L.lbv_moe_forward_fp8.argtypes = [C, I64, P, P, P, P, ctypes.POINTER(_Fp8WeightsC), P, P, P,
                                       P, SZ, P]
     L.lbv_moe_forward_fp8.restype = st
+    A = ctypes.POINTER(AttnConfig)
+    L.lbv_attn_workspace_size.argtypes = [A, I64, I64, ctypes.POINTER(SZ)]
+    L.lbv_attn_workspace_size.restype = st
+    L.lbv_linear_bf16.argtypes = [I64, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P, SZ, P]
+    L.lbv_linear_bf16.restype = st
+    L.lbv_attn_qk_prep.argtypes = [A, I64, I64, P, P, P, P, P, P, P, P, P]
+    L.lbv_attn_qk_prep.restype = st
+    L.lbv_attn_core.argtypes = [A, I64, I64, P, P, P, P, P, P]
+    L.lbv_attn_core.restype = st
+    L.lbv_attn_forward.argtypes = [A, I64, I64, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    L.lbv_attn_forward.restype = st
     _lib = L
     return L
 
@@ -537,6 +569,78 @@ def lbv_moe_forward_fp8(cfg, x, mask, router_w, e_bias, wq: Fp8Weights, out, top
         ctypes.byref(cw), _ptr(out, "out", dt), _ptr(topk_ids_out, "topk_ids_out", torch.int32),
         _ptr(topk_w_out, "topk_w_out", torch.float32), _ptr(ws, "ws"),
         ws.numel() * ws.element_size(), _stream(stream)), "lbv_moe_forward_fp8")
+
+
+def lbv_attn_workspace_size(cfg: AttnConfig, B: int, S: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().lbv_attn_workspace_size(ctypes.byref(cfg), B, S, ctypes.byref(n)),
+           "lbv_attn_workspace_size")
+    return n.value
+
+
+LINEAR_WS_BYTES = 512
+
+
+def lbv_linear_bf16(x, w, bias, y, ws, stream=None):
+    """y [T, N] = x [T, K] w[N, K]^T (+ bias [N] fp32), bf16."""
+    _shape(x, "x", None, None)
+    T, K = x.shape
+    _shape(w, "w", None, K)
+    N = w.shape[0]
+    _shape(bias, "bias", N)
+    _shape(y, "y", T, N)
+    _need(ws, "ws")
+    _numel_at_least(ws, "ws", LINEAR_WS_BYTES)
+    _same_device(x, w, bias, y, ws)
+    _check(load().lbv_linear_bf16(
+        T, N, K, _ptr(x, "x", torch.bfloat16), _ptr(w, "w", torch.bfloat16),
+        _ptr(bias, "bias", torch.float32), _ptr(y, "y", torch.bfloat16), _ptr(ws, "ws"),
+        ws.numel() * ws.element_size(), _stream(stream)), "lbv_linear_bf16")
+
+
+def _attn_shapes(cfg, B, S, **ts):
+    H, D = cfg.hidden, cfg.head_dim
+    T = B * S
+    want = dict(x=(T, H), qkv=(T, 3 * H), q=(T, H), k=(T, H), o=(T, H), out=(T, H),
+                vt=(B, cfg.num_heads, D, attn_sp(S)), mask=(T,), g_q=(D,), g_k=(D,),
+                cos=(T, D // 2), sin=(T, D // 2), w_qkv=(3 * H, H), b_qkv=(3 * H,), w_o=(H, H),
+                b_o=(H,))
+    for name, t in ts.items():
+        _shape(t, name, *want[name])
+
+
+def lbv_attn_qk_prep(cfg, B, S, qkv, g_q, g_k, cos, sin, q, k, vt, stream=None):
+    _attn_shapes(cfg, B, S, qkv=qkv, g_q=g_q, g_k=g_k, cos=cos, sin=sin, q=q, k=k, vt=vt)
+    _same_device(qkv, g_q, g_k, cos, sin, q, k, vt)
+    bf, f = torch.bfloat16, torch.float32
+    _check(load().lbv_attn_qk_prep(
+        ctypes.byref(cfg), B, S, _ptr(qkv, "qkv", bf), _ptr(g_q, "g_q", f), _ptr(g_k, "g_k", f),
+        _ptr(cos, "cos", f), _ptr(sin, "sin", f), _ptr(q, "q", bf), _ptr(k, "k", bf),
+        _ptr(vt, "vt", bf), _stream(stream)), "lbv_attn_qk_prep")
+
+
+def lbv_attn_core(cfg, B, S, q, k, vt, mask, o, stream=None):
+    _attn_shapes(cfg, B, S, q=q, k=k, vt=vt, mask=mask, o=o)
+    _same_device(q, k, vt, mask, o)
+    bf = torch.bfloat16
+    _check(load().lbv_attn_core(
+        ctypes.byref(cfg), B, S, _ptr(q, "q", bf), _ptr(k, "k", bf), _ptr(vt, "vt", bf),
+        _ptr(mask, "mask", torch.uint8), _ptr(o, "o", bf), _stream(stream)), "lbv_attn_core")
+
+
+def lbv_attn_forward(cfg, B, S, x, mask, w_qkv, b_qkv, g_q, g_k, cos, sin, w_o, b_o, out, ws,
+                     stream=None):
+    _attn_shapes(cfg, B, S, x=x, mask=mask, w_qkv=w_qkv, b_qkv=b_qkv, g_q=g_q, g_k=g_k, cos=cos,
+                 sin=sin, w_o=w_o, b_o=b_o, out=out)
+    _need(ws, "ws")
+    _same_device(x, mask, w_qkv, b_qkv, g_q, g_k, cos, sin, w_o, b_o, out, ws)
+    bf, f = torch.bfloat16, torch.float32
+    _check(load().lbv_attn_forward(
+        ctypes.byref(cfg), B, S, _ptr(x, "x", bf), _ptr(mask, "mask", torch.uint8),
+        _ptr(w_qkv, "w_qkv", bf), _ptr(b_qkv, "b_qkv", f), _ptr(g_q, "g_q", f),
+        _ptr(g_k, "g_k", f), _ptr(cos, "cos", f), _ptr(sin, "sin", f), _ptr(w_o, "w_o", bf),
+        _ptr(b_o, "b_o", f), _ptr(out, "out", bf), _ptr(ws, "ws"),
+        ws.numel() * ws.element_size(), _stream(stream)), "lbv_attn_forward")
 
 
 class MoEBlock:

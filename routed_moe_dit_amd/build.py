@@ -17,7 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "liblbv_moe.so")
-SOURCES = ["route.hip", "permute.hip", "gemm.hip", "adaln.hip", "quant.hip", "abi.cpp"]
+SOURCES = ["route.hip", "permute.hip", "gemm.hip", "adaln.hip", "quant.hip", "attn.hip",
+           "abi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

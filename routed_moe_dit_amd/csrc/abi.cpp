@@ -13,7 +13,7 @@ using lbv::Dims;
 
 namespace {
 
-constexpr int32_t kAbiVersion = 3;
+constexpr int32_t kAbiVersion = 4;
 constexpr size_t kAlign = 256;
 
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -499,6 +499,139 @@ lbv_status lbv_moe_forward(const lbv_moe_config* cfg, int64_t T, const void* x,
         e = lbv::launch_gemm_w2(d, act, w2, shared_w2, offsets, sorted, y, ctr2, stream, nullptr,
                                 nullptr, false);
     if (e == hipSuccess) e = lbv::launch_combine(d, y, inv, w, out, stream);
+    return hip_status(e);
+}
+
+}  // extern "C"
+
+// ---- attention half ----------------------------------------------------------
+
+namespace {
+
+constexpr int kHeadDim = 128;
+
+lbv_status check_attn(const lbv_attn_config* c, int64_t B, int64_t S) {
+    if (!c) return LBV_ERR_NULL;
+    if (c->num_heads <= 0 || c->hidden != c->num_heads * kHeadDim) return LBV_ERR_UNSUPPORTED;
+    if (!(c->eps >= 0.0f) || !isfinite(c->eps)) return LBV_ERR_SHAPE;
+    if (B < 0 || S < 0 || S > 65536) return LBV_ERR_SHAPE;
+    const int64_t T = B * S;
+    if (B > 0 && S > 0 && (T >= (1 << 24) || T * 3 * c->hidden * 2 >= (1ll << 32) ||
+                           int64_t(c->hidden) * 3 * c->hidden * 2 >= (1ll << 32)))
+        return LBV_ERR_SHAPE;
+    return LBV_OK;
+}
+
+struct AttnLayout {
+    size_t lin, qkv, q, k, vt, o, total;
+};
+
+AttnLayout attn_layout(const lbv_attn_config* c, int64_t B, int64_t S) {
+    AttnLayout L;
+    const size_t T = static_cast<size_t>(B * S), H = static_cast<size_t>(c->hidden);
+    size_t off = 0;
+    L.lin = off; off += round_up(lbv::kLinearWsBytes);
+    L.qkv = off; off += round_up(T * 3 * H * 2);
+    L.q = off;   off += round_up(T * H * 2);
+    L.k = off;   off += round_up(T * H * 2);
+    L.vt = off;  off += round_up(static_cast<size_t>(B) * H * lbv::attn_sp(static_cast<int>(S)) * 2);
+    L.o = off;   off += round_up(T * H * 2);
+    L.total = off;
+    return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+lbv_status lbv_attn_workspace_size(const lbv_attn_config* cfg, int64_t B, int64_t S,
+                                   size_t* bytes) {
+    if (!bytes) return LBV_ERR_NULL;
+    lbv_status st = check_attn(cfg, B, S);
+    if (st != LBV_OK) return st;
+    *bytes = attn_layout(cfg, B, S).total;
+    return LBV_OK;
+}
+
+lbv_status lbv_linear_bf16(int64_t T, int32_t N, int32_t K, const void* x, const void* w,
+                           const float* bias, void* y, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+    if (T < 0 || N <= 0 || K <= 0 || N % 64 != 0 || K % 64 != 0) return LBV_ERR_SHAPE;
+    if (T >= (1 << 24) || T * K * 2 >= (1ll << 32) || int64_t(N) * K * 2 >= (1ll << 32) ||
+        N >= (1 << 24) || K >= (1 << 24))
+        return LBV_ERR_SHAPE;
+    if (T == 0) return LBV_OK;
+    if (!x || !w || !y || !ws) return LBV_ERR_NULL;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y) || !aligned16(ws) || !aligned4(bias))
+        return LBV_ERR_ALIGN;
+    if (ws_bytes < lbv::kLinearWsBytes) return LBV_ERR_WORKSPACE;
+    const size_t xb = static_cast<size_t>(T) * K * 2, yb = static_cast<size_t>(T) * N * 2;
+    if (overlaps(x, xb, y, yb) || overlaps(w, static_cast<size_t>(N) * K * 2, y, yb) ||
+        overlaps(ws, lbv::kLinearWsBytes, y, yb))
+        return LBV_ERR_ALIAS;
+    return hip_status(lbv::launch_linear(T, N, K, x, w, bias, y, ws, stream));
+}
+
+lbv_status lbv_attn_qk_prep(const lbv_attn_config* cfg, int64_t B, int64_t S, const void* qkv,
+                            const float* g_q, const float* g_k, const float* cos_t,
+                            const float* sin_t, void* q, void* k, void* vt, hipStream_t stream) {
+    lbv_status st = check_attn(cfg, B, S);
+    if (st != LBV_OK) return st;
+    if (B == 0 || S == 0) return LBV_OK;
+    if (!qkv || !g_q || !g_k || !cos_t || !sin_t || !q || !k || !vt) return LBV_ERR_NULL;
+    if (!aligned16(qkv) || !aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned4(g_q) ||
+        !aligned4(g_k) || !aligned4(cos_t) || !aligned4(sin_t))
+        return LBV_ERR_ALIGN;
+    return hip_status(lbv::launch_attn_prep(static_cast<int>(B), static_cast<int>(S), cfg->hidden,
+                                            cfg->num_heads, qkv, g_q, g_k, cos_t, sin_t, cfg->eps,
+                                            q, k, vt, stream));
+}
+
+lbv_status lbv_attn_core(const lbv_attn_config* cfg, int64_t B, int64_t S, const void* q,
+                         const void* k, const void* vt, const uint8_t* mask, void* o,
+                         hipStream_t stream) {
+    lbv_status st = check_attn(cfg, B, S);
+    if (st != LBV_OK) return st;
+    if (B == 0 || S == 0) return LBV_OK;
+    if (!q || !k || !vt || !o) return LBV_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o)) return LBV_ERR_ALIGN;
+    return hip_status(lbv::launch_attn_core(static_cast<int>(B), static_cast<int>(S), cfg->hidden,
+                                            cfg->num_heads, q, k, vt, mask, o, stream));
+}
+
+lbv_status lbv_attn_forward(const lbv_attn_config* cfg, int64_t B, int64_t S, const void* x,
+                            const uint8_t* mask, const void* w_qkv, const float* b_qkv,
+                            const float* g_q, const float* g_k, const float* cos_t,
+                            const float* sin_t, const void* w_o, const float* b_o, void* out,
+                            void* ws, size_t ws_bytes, hipStream_t stream) {
+    lbv_status st = check_attn(cfg, B, S);
+    if (st != LBV_OK) return st;
+    if (B == 0 || S == 0) return LBV_OK;
+    if (!x || !w_qkv || !g_q || !g_k || !cos_t || !sin_t || !w_o || !out || !ws)
+        return LBV_ERR_NULL;
+    if (!aligned16(x) || !aligned16(w_qkv) || !aligned16(w_o) || !aligned16(out) ||
+        !aligned16(ws) || !aligned4(b_qkv) || !aligned4(b_o) || !aligned4(g_q) ||
+        !aligned4(g_k) || !aligned4(cos_t) || !aligned4(sin_t))
+        return LBV_ERR_ALIGN;
+    const AttnLayout L = attn_layout(cfg, B, S);
+    if (ws_bytes < L.total) return LBV_ERR_WORKSPACE;
+    const int64_t T = B * S;
+    const int H = cfg->hidden;
+    const size_t xb = static_cast<size_t>(T) * H * 2;
+    if (overlaps(x, xb, out, xb) || overlaps(ws, ws_bytes, out, xb) || overlaps(ws, ws_bytes, x, xb))
+        return LBV_ERR_ALIAS;
+    char* base = static_cast<char*>(ws);
+    hipError_t e = lbv::launch_linear(T, 3 * H, H, x, w_qkv, b_qkv, base + L.qkv, base + L.lin,
+                                      stream);
+    if (e == hipSuccess)
+        e = lbv::launch_attn_prep(static_cast<int>(B), static_cast<int>(S), H, cfg->num_heads,
+                                  base + L.qkv, g_q, g_k, cos_t, sin_t, cfg->eps, base + L.q,
+                                  base + L.k, base + L.vt, stream);
+    if (e == hipSuccess)
+        e = lbv::launch_attn_core(static_cast<int>(B), static_cast<int>(S), H, cfg->num_heads,
+                                  base + L.q, base + L.k, base + L.vt, mask, base + L.o, stream);
+    if (e == hipSuccess)
+        e = lbv::launch_linear(T, H, H, base + L.o, w_o, b_o, out, base + L.lin, stream);
     return hip_status(e);
 }
 

@@ -118,6 +118,7 @@ struct GemmArgs {
     const void* Bsh;        // gate/up: shared_w13 [2 Is, H];  down: shared_w2 [H, Is]
     const float* Bs;        // fp8 weights: row scales of B ([E, 2I] / [E, H])
     const float* Bshs;      // fp8 weights: row scales of Bsh ([2 Is] / [H])
+    const float* bias;      // dense down-style matmul: [ncols] fp32 added before rounding, or null
     const int32_t* offsets; // [S + 1]
     const int32_t* rows;    // sorted_rows: slot id of each sorted row
     void* C;                // gate/up: act [rows, I];  down: y [rows, H]
@@ -197,8 +198,12 @@ constexpr int kMaxSeg = 512;
 // once, then runs one continuous k-loop over all its tiles: the copies of the
 // next tile's first STG-1 k-tiles are issued during the current tile's last
 // k-tiles and land while its epilogue runs.
-template <int BM, int BN, int MODE, int NW, int CWV, int ORDER, int STG, bool W8>
+// DENSE (down-style only): one segment whose rows are stored in order (no
+// slot ids) and an optional fp32 bias per output column: a plain linear layer
+// y = x W^T + b.
+template <int BM, int BN, int MODE, int NW, int CWV, int ORDER, int STG, bool W8, bool DENSE>
 __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
+    static_assert(!DENSE || MODE == 1, "dense rows: down-style only");
     // NW waves: 2 along the tokens x NW/2 along the weight rows (NW = 4: one
     // wave per SIMD with 128 x 128 accumulators; NW = 8: two per SIMD with
     // 128 x 64, so that one wave's MFMAs can cover the other's waits).
@@ -675,7 +680,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         const bool do_copy = want && kc < nk;    // past nk it is a zero-filled stage
         if (want && kc >= nk) zero_fill(TS);
         if (MODE == 0 && kt == 0 && has_next) rid_copy(nseg_r0, nseg_n, nm0);
-        if (MODE == 1 && kt == 0) rid_copy(seg_r0, seg_n, m0);
+        if (MODE == 1 && !DENSE && kt == 0) rid_copy(seg_r0, seg_n, m0);
 #pragma unroll
         for (int kk = 0; kk < KKS - 1; ++kk) {
             conv(kk);
@@ -790,6 +795,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
                                 v[e] = g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
                             } else {
                                 v[e] = acc[j][i][4 * q + e];
+                                if (DENSE && a.bias) {
+                                    const int bc = col0 + col + e;
+                                    v[e] += a.bias[bc < ncols_all ? bc : ncols_all - 1];
+                                }
                             }
                         }
                         uint2 o;
@@ -811,7 +820,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
                 const int col = col0 + ch * 8;
                 const u32x4 v = *reinterpret_cast<const u32x4*>(ep + ep_off(row, ch * 8));
                 // gate/up: act rows in segment order; down: y rows in slot order
-                const int64_t orow = MODE == 0 ? seg_r0 + m : s_rid[wm * (BM / 2) + p * PROWS + row];
+                const int64_t orow = MODE == 0 || DENSE ? seg_r0 + m : s_rid[wm * (BM / 2) + p * PROWS + row];
                 if (m < seg_n && col >= lo && col <= hi) {
                     u32x4* dst = reinterpret_cast<u32x4*>(C + orow * ncols + col);
                     if (MODE == 0 ? LBV_G1_EPI_NT : LBV_G2_EPI_NT) __builtin_nontemporal_store(v, dst);
@@ -1095,20 +1104,20 @@ int64_t max_mtiles(const Dims& d, int BM) {
 template <bool W8>
 void launch_w13_bf16(const Dims& d, const GemmArgs& a, hipStream_t stream) {
     if (few_rows(d))
-        hipLaunchKernelGGL((gemm_bf16_kernel<64, G1_BN, 0, LBV_G1_WAVES, LBV_G1_COPY_WAVES, LBV_G1_ORDER, LBV_FEW_STAGES, W8>),
+        hipLaunchKernelGGL((gemm_bf16_kernel<64, G1_BN, 0, LBV_G1_WAVES, LBV_G1_COPY_WAVES, LBV_G1_ORDER, LBV_FEW_STAGES, W8, false>),
                            dim3(cu_count() / 8 * 8), dim3(LBV_G1_WAVES * 64), 0, stream, a);
     else
-        hipLaunchKernelGGL((gemm_bf16_kernel<G1_BM, G1_BN, 0, LBV_G1_WAVES, LBV_G1_COPY_WAVES, LBV_G1_ORDER, 2, W8>),
+        hipLaunchKernelGGL((gemm_bf16_kernel<G1_BM, G1_BN, 0, LBV_G1_WAVES, LBV_G1_COPY_WAVES, LBV_G1_ORDER, 2, W8, false>),
                            dim3(cu_count() / 8 * 8), dim3(LBV_G1_WAVES * 64), 0, stream, a);
 }
 
 template <bool W8>
 void launch_w2_bf16(const Dims& d, const GemmArgs& a, hipStream_t stream) {
     if (few_rows(d))
-        hipLaunchKernelGGL((gemm_bf16_kernel<64, G2_BN, 1, LBV_G2_WAVES, LBV_G2_COPY_WAVES, LBV_G2_ORDER, LBV_FEW_STAGES, W8>),
+        hipLaunchKernelGGL((gemm_bf16_kernel<64, G2_BN, 1, LBV_G2_WAVES, LBV_G2_COPY_WAVES, LBV_G2_ORDER, LBV_FEW_STAGES, W8, false>),
                            dim3(cu_count() / 8 * 8), dim3(LBV_G2_WAVES * 64), 0, stream, a);
     else
-        hipLaunchKernelGGL((gemm_bf16_kernel<G2_BM, G2_BN, 1, LBV_G2_WAVES, LBV_G2_COPY_WAVES, LBV_G2_ORDER, 2, W8>),
+        hipLaunchKernelGGL((gemm_bf16_kernel<G2_BM, G2_BN, 1, LBV_G2_WAVES, LBV_G2_COPY_WAVES, LBV_G2_ORDER, 2, W8, false>),
                            dim3(cu_count() / 8 * 8), dim3(LBV_G2_WAVES * 64), 0, stream, a);
 }
 
@@ -1171,6 +1180,50 @@ hipError_t launch_gemm_w2(const Dims& d, const void* act, const void* w2, const 
         hipLaunchKernelGGL(gemm_f32_kernel<1>, dim3(static_cast<unsigned>(grid)), dim3(256), 0,
                            stream, a);
     }
+    return hipGetLastError();
+}
+
+namespace {
+// offsets of the one segment ([0, T]) and zeroed tile-queue counters
+__global__ __launch_bounds__(64) void dense_setup_kernel(int32_t* offsets, int* ctr, int T) {
+    const int l = threadIdx.x;
+    if (l < 2) offsets[l] = l == 0 ? 0 : T;
+    if (l < 8) ctr[l] = 0;
+}
+}  // namespace
+
+hipError_t launch_linear(int64_t T, int N, int K, const void* x, const void* w, const float* bias,
+                         void* y, void* ws, hipStream_t stream) {
+    GemmArgs a{};
+    a.T = T;
+    a.H = N;
+    a.I = K;
+    a.E = 1;
+    a.NS = 0;
+    a.KS = 1;
+    a.S = 1;
+    a.A = x;
+    a.B = w;
+    a.Bsh = w;
+    a.bias = bias;
+    int32_t* offsets = static_cast<int32_t*>(ws);
+    a.offsets = offsets;
+    a.rows = nullptr;
+    a.ctr = reinterpret_cast<int*>(static_cast<char*>(ws) + 256);
+    a.C = y;
+    a.kdim = K;
+    a.ncols = N;
+    a.ntn = (N + G2_BN - 1) / G2_BN;
+    hipLaunchKernelGGL(dense_setup_kernel, dim3(1), dim3(64), 0, stream, offsets, a.ctr,
+                       static_cast<int>(T));
+    // 64-row tiles when 256-row ones would not give every CU a tile
+    const int64_t tiles256 = (T + 255) / 256 * a.ntn;
+    if (tiles256 < cu_count())
+        hipLaunchKernelGGL((gemm_bf16_kernel<64, G2_BN, 1, LBV_G2_WAVES, LBV_G2_COPY_WAVES, LBV_G2_ORDER, LBV_FEW_STAGES, false, true>),
+                           dim3(cu_count() / 8 * 8), dim3(LBV_G2_WAVES * 64), 0, stream, a);
+    else
+        hipLaunchKernelGGL((gemm_bf16_kernel<G2_BM, G2_BN, 1, LBV_G2_WAVES, LBV_G2_COPY_WAVES, LBV_G2_ORDER, 2, false, true>),
+                           dim3(cu_count() / 8 * 8), dim3(LBV_G2_WAVES * 64), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -93,6 +93,22 @@ hipError_t launch_quantize_fp8(const void* w, int src_bf16, int64_t rows, int co
 hipError_t launch_combine(const Dims& d, const void* y, const int32_t* inv_rows,
                           const float* topk_w, void* out, hipStream_t stream);
 
+// Dense bf16 linear y [T, N] = x [T, K] W[N, K]^T (+ bias [N] fp32), rounded
+// once to bf16, on the grouped matmul kernel with one segment; ws: 512 bytes
+// (segment offsets and tile-queue counters, set on the stream).
+constexpr size_t kLinearWsBytes = 512;
+hipError_t launch_linear(int64_t T, int N, int K, const void* x, const void* w, const float* bias,
+                         void* y, void* ws, hipStream_t stream);
+
+// Attention half (head dim 128): q/k norms + rotary embedding + v transposed
+// into vt [B][heads][128][attn_sp(S)], then masked per-sample attention.
+int attn_sp(int S);
+hipError_t launch_attn_prep(int B, int S, int H, int heads, const void* qkv, const float* gq,
+                            const float* gk, const float* cs, const float* sn, float eps, void* q,
+                            void* k, void* vt, hipStream_t stream);
+hipError_t launch_attn_core(int B, int S, int H, int heads, const void* q, const void* k,
+                            const void* vt, const uint8_t* mask, void* o, hipStream_t stream);
+
 // AdaLN in front of the block and the gated residual after it.
 struct AdalnArgs {
     const float* x;        // [T, H] fp32 residual stream

@@ -34,6 +34,8 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "by_name", "make_inputs", "round_to_bf16",
     "bf16_bits", "bits_to_f32", "digest", "token_mask", "random_act", "make_adaln_inputs",
+    "AttnWorkload", "ATTN_WORKLOADS", "attn_by_name", "make_attn_inputs", "joint_positions",
+    "rope_tables",
 ]
 
 
@@ -237,3 +239,114 @@ def digest(inputs: dict) -> dict:
         else:
             out[k] = hashlib.sha256(np.ascontiguousarray(v).tobytes()).hexdigest()[:16]
     return out
+
+
+# ---------------------------------------------------------------------------
+# The attention half of a DiT layer (prhub summary of sglang PR #32341,
+# LingBotVideoAttention under "关键源码片段"; "实现拆解" step 2: video;text
+# joint attention with 3D joint position ids, padding isolated by the mask).
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class AttnWorkload:
+    """B samples of S tokens (padding included); each sample is a video part
+    on a latent token grid (frames x rows x columns) followed by text tokens,
+    with `valid[b]` real tokens and padding after them."""
+
+    name: str
+    B: int
+    S: int
+    grid: Tuple[int, int, int]
+    text: int
+    valid: Tuple[int, ...]
+    hidden: int
+    heads: int
+    seed: int
+    x_std: float = 1.0
+    b_std: float = 0.02
+    g_std: float = 0.1
+    theta: float = 10000.0
+
+    @property
+    def T(self) -> int:
+        return self.B * self.S
+
+    @property
+    def head_dim(self) -> int:
+        return self.hidden // self.heads
+
+
+ATTN_WORKLOADS = (
+    # 9 frames at 192x320: a 3 x 12 x 20 grid (720 tokens) + 80 text tokens
+    AttnWorkload("attn_smoke_T800", B=1, S=800, grid=(3, 12, 20), text=80, valid=(800,),
+                 hidden=2048, heads=16, seed=21),
+    # the classifier-free-guidance pair, 40 padding tokens at the end of sample 2
+    AttnWorkload("attn_cfg_B2_T1600", B=2, S=800, grid=(3, 12, 20), text=80, valid=(800, 760),
+                 hidden=2048, heads=16, seed=22),
+    # 81 frames at 480x480: a 21 x 30 x 30 grid (18,900 tokens) + 100 text, B = 2
+    AttnWorkload("attn_default_B2_T38000", B=2, S=19000, grid=(21, 30, 30), text=100,
+                 valid=(19000, 19000), hidden=2048, heads=16, seed=23),
+)
+
+
+def attn_by_name(name: str) -> AttnWorkload:
+    for w in ATTN_WORKLOADS:
+        if w.name == name:
+            return w
+    raise KeyError(name)
+
+
+def joint_positions(aw: AttnWorkload) -> np.ndarray:
+    """int32 [T, 3] positions (frame, row, column) of every token: video tokens
+    in raster order of their grid cell, text token j at (frames + j, 0, 0),
+    padding at (0, 0, 0)."""
+    F, R, C = aw.grid
+    f, r, c = np.meshgrid(np.arange(F), np.arange(R), np.arange(C), indexing="ij")
+    video = np.stack([f.ravel(), r.ravel(), c.ravel()], 1)
+    text = np.stack([F + np.arange(aw.text), np.zeros(aw.text, int), np.zeros(aw.text, int)], 1)
+    sample = np.concatenate([video, text]).astype(np.int32)
+    assert len(sample) <= aw.S
+    pos = np.zeros((aw.T, 3), np.int32)
+    for b in range(aw.B):
+        n = min(len(sample), aw.valid[b])
+        pos[b * aw.S:b * aw.S + n] = sample[:n]
+    return pos
+
+
+def rope_tables(aw: AttnWorkload) -> Tuple[np.ndarray, np.ndarray]:
+    """cos, sin fp32 [T, D/2] for the 3D positions: the D/2 channel pairs are
+    split into (time, row, column) blocks of D/2 - 2 (D/6), D/6, D/6 pairs
+    (Wan's split), pair j of a block of n turning by pos * theta^(-j / n)."""
+    D = aw.head_dim
+    nh = D // 6
+    n = (D // 2 - 2 * nh, nh, nh)
+    pos = joint_positions(aw).astype(np.float64)
+    ang = np.concatenate([np.outer(pos[:, a], aw.theta ** (-np.arange(n[a]) / n[a]))
+                          for a in range(3)], 1)
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def make_attn_inputs(aw: AttnWorkload) -> dict:
+    """The attention half's inputs (one stream, seed aw.seed): ``x [T, H]`` the
+    modulated layer input (bf16 values), ``w_qkv [3H, H]`` (q, k, v rows) and
+    ``w_o [H, H]`` (bf16 values, std H^-1/2), the biases ``b_qkv [3H]`` and
+    ``b_o [H]`` (fp32, std b_std), the q / k norm weights ``g_q, g_k [D]``
+    (fp32, 1 + N(0, g_std^2)), the rotary tables ``cos, sin [T, D/2]`` and the
+    mask (u8 [T], or None when every token is valid)."""
+    T, H, D = aw.T, aw.hidden, aw.head_dim
+    rng = np.random.default_rng(aw.seed)
+    x = round_to_bf16(_draw(rng, (T, H), aw.x_std))
+    w_qkv = round_to_bf16(_draw(rng, (3 * H, H), H ** -0.5))
+    b_qkv = _draw(rng, (3 * H,), aw.b_std)
+    g_q = 1 + _draw(rng, (D,), aw.g_std)
+    g_k = 1 + _draw(rng, (D,), aw.g_std)
+    w_o = round_to_bf16(_draw(rng, (H, H), H ** -0.5))
+    b_o = _draw(rng, (H,), aw.b_std)
+    cos, sin = rope_tables(aw)
+    mask = None
+    if any(v < aw.S for v in aw.valid):
+        mask = np.zeros(T, np.uint8)
+        for b, v in enumerate(aw.valid):
+            mask[b * aw.S:b * aw.S + v] = 1
+    return dict(x=x, w_qkv=w_qkv, b_qkv=b_qkv, g_q=g_q, g_k=g_k, w_o=w_o, b_o=b_o, cos=cos,
+                sin=sin, mask=mask)

@@ -21,7 +21,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 19, names
+    assert len(names) == 24, names
     assert set(names) == set(lbv.EXPORTS)
     L = ctypes.CDLL(lbv.LIB_PATH)
     for n in names:
@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert lbv.lbv_abi_version() == 3
+    assert lbv.lbv_abi_version() == 4
     texts = {lbv.lbv_status_string(s) for s in range(9)}
     assert len(texts) == 9
     assert lbv.lbv_status_string(99) == "unknown status"
@@ -400,3 +400,39 @@ def test_fp8_binding_shape_checks():
         lbv.lbv_quantize_fp8_rows(w.half(), torch.zeros(4, 64, dtype=torch.uint8), torch.zeros(4))
     with pytest.raises(ValueError, match="device tensor"):
         lbv.lbv_quantize_fp8_rows(w, torch.zeros(4, 64, dtype=torch.uint8), torch.zeros(4))
+
+
+def test_attention_validation_paths():
+    """The attention entries reject before any launch."""
+    L = raw()
+    c = lbv.attn_config()
+    need = lbv.lbv_attn_workspace_size(c, 2, 800)
+    T, H = 1600, 2048
+    # 512 bytes, qkv, q, k, o, and vt with S rounded up to 832 key positions
+    assert need == 512 + T * 3 * H * 2 + 3 * T * H * 2 + 2 * H * 832 * 2
+    bad = lbv.AttnConfig(2048, 8, 1e-6)                      # head dim 256
+    n = ctypes.c_size_t()
+    assert L.lbv_attn_workspace_size(ctypes.byref(bad), 1, 8, ctypes.byref(n)) == \
+        lbv.LBV_ERR_UNSUPPORTED
+    assert L.lbv_attn_workspace_size(ctypes.byref(c), 1, 65537, ctypes.byref(n)) == \
+        lbv.LBV_ERR_SHAPE
+    neg = lbv.AttnConfig(2048, 16, -1.0)
+    assert L.lbv_attn_workspace_size(ctypes.byref(neg), 1, 8, ctypes.byref(n)) == \
+        lbv.LBV_ERR_SHAPE
+
+    def f(B=2, S=800, x=A, out=Cc, ws=BIG, ws_bytes=need, cfg=c):
+        return L.lbv_attn_forward(ctypes.byref(cfg), B, S, x, None, B_, None, A, A, A, A, B_, None,
+                                  out, ws, ws_bytes, None)
+    B_ = B
+    assert f(B=0) == lbv.LBV_OK
+    assert f(x=None) == lbv.LBV_ERR_NULL
+    assert f(out=Cc + 8) == lbv.LBV_ERR_ALIGN
+    assert f(ws_bytes=need - 1) == lbv.LBV_ERR_WORKSPACE
+    assert f(out=A + 64) == lbv.LBV_ERR_ALIAS
+    assert L.lbv_linear_bf16(8, 100, 64, A, B, None, Cc, BIG, 512, None) == lbv.LBV_ERR_SHAPE
+    assert L.lbv_linear_bf16(8, 128, 64, A, B, None, Cc, BIG, 511, None) == lbv.LBV_ERR_WORKSPACE
+    assert L.lbv_linear_bf16(0, 128, 64, None, None, None, None, None, 0, None) == lbv.LBV_OK
+    assert L.lbv_linear_bf16(8, 128, 64, A, B, None, A + 16, BIG, 512, None) == lbv.LBV_ERR_ALIAS
+    assert L.lbv_attn_core(ctypes.byref(c), 1, 8, A, B, None, None, Cc, None) == lbv.LBV_ERR_NULL
+    assert L.lbv_attn_qk_prep(ctypes.byref(c), 1, 8, A, A, A, A, A, B, Cc, BIG + 8, None) == \
+        lbv.LBV_ERR_ALIGN
