@@ -53,6 +53,9 @@ def parse():
     p.add_argument("--fp8", action="store_true",
                    help="also time the block with fp8 (e4m3fn, per-row power-of-two scale) "
                         "expert weights (lbv_moe_forward_fp8) and the device quantizer")
+    p.add_argument("--attn", action="store_true",
+                   help="also time the attention half of the layer (lbv_attn_forward) on the "
+                        "attention workload of the same token layout, and its kernels")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after the measurements, run a plain 1 GiB device copy three times, so "
                         "that a hardware-counter run can scale its byte counters")
@@ -359,6 +362,75 @@ def main():
                       "activations, fp32 accumulation",
         }
         del wq
+
+    # ---- the attention half of the layer on the same token layout -----------------
+    if args.attn and bf:
+        aw = [a for a in synth.ATTN_WORKLOADS if a.T == T]
+        if aw:
+            aw = aw[0]
+            ai = synth.make_attn_inputs(aw)
+            acfg = lbv.attn_config(hidden=aw.hidden, num_heads=aw.heads, eps=1e-6)
+            ad = {k_: (dev(v_, k_ in ("x", "w_qkv", "w_o")) if v_ is not None and v_.dtype == np.float32
+                       else (None if v_ is None else torch.from_numpy(v_).cuda()))
+                  for k_, v_ in ai.items()}
+            del ai
+            B_, S_ = aw.B, aw.S
+            aout = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+            aws = torch.empty(lbv.lbv_attn_workspace_size(acfg, B_, S_), dtype=torch.uint8,
+                              device="cuda")
+            lws = torch.empty(lbv.LINEAR_WS_BYTES, dtype=torch.uint8, device="cuda")
+            qkv = torch.empty(T, 3 * H, dtype=torch.bfloat16, device="cuda")
+            aq, ak, ao = (torch.empty(T, H, dtype=torch.bfloat16, device="cuda") for _ in range(3))
+            avt = torch.empty(B_, aw.heads, 128, lbv.attn_sp(S_), dtype=torch.bfloat16,
+                              device="cuda")
+
+            def half():
+                lbv.lbv_attn_forward(acfg, B_, S_, ad["x"], ad["mask"], ad["w_qkv"], ad["b_qkv"],
+                                     ad["g_q"], ad["g_k"], ad["cos"], ad["sin"], ad["w_o"],
+                                     ad["b_o"], aout, aws, stream)
+
+            def timed_n(fn, n):
+                for _ in range(2):
+                    fn()
+                torch.cuda.synchronize()
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+                e[0].record(stream)
+                for i in range(n):
+                    fn()
+                    e[i + 1].record(stream)
+                torch.cuda.synchronize()
+                return [e[i].elapsed_time(e[i + 1]) for i in range(n)]
+
+            nrep = max(5, min(args.steps, 20))
+            h_ms = timed_n(half, nrep)
+            parts = {
+                "qkv_proj": lambda: lbv.lbv_linear_bf16(ad["x"], ad["w_qkv"], ad["b_qkv"], qkv, lws,
+                                                        stream),
+                "qk_prep": lambda: lbv.lbv_attn_qk_prep(acfg, B_, S_, qkv, ad["g_q"], ad["g_k"],
+                                                        ad["cos"], ad["sin"], aq, ak, avt, stream),
+                "attention": lambda: lbv.lbv_attn_core(acfg, B_, S_, aq, ak, avt, ad["mask"], ao,
+                                                       stream),
+                "out_proj": lambda: lbv.lbv_linear_bf16(ao, ad["w_o"], ad["b_o"], aout, lws,
+                                                        stream),
+            }
+            part_ms = {k_: float(np.median(timed_n(f_, nrep))) for k_, f_ in parts.items()}
+            valid = [min(v_, S_) for v_ in aw.valid]
+            attn_flops = 4.0 * sum(v_ * v_ for v_ in valid) * H      # QK^T and PV, valid tokens
+            a_s = part_ms["attention"] * 1e-3
+            res["attention_half"] = {
+                "workload": aw.name,
+                "ms": float(np.median(h_ms)),
+                "tokens_per_s": T / (float(np.median(h_ms)) * 1e-3),
+                "stage_ms": part_ms,
+                "qkv_proj_tflops": 2.0 * T * 3 * H * H / (part_ms["qkv_proj"] * 1e-3) / 1e12,
+                "out_proj_tflops": 2.0 * T * H * H / (part_ms["out_proj"] * 1e-3) / 1e12,
+                "roofline": {"kernel": "attn_fwd_kernel (lbv_attn_core)", "bound": "mfma",
+                             "achieved": attn_flops / a_s / 1e12, "peak": BF16_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": attn_flops / a_s / 1e12 / BF16_PEAK_TFLOPS,
+                             "algorithmic_flops_per_launch": attn_flops, "traffic": None},
+                "layout": "B=%d samples of S=%d tokens, %d heads of 128" % (B_, S_, aw.heads),
+            }
+            del ad, aout, aws, qkv, aq, ak, ao, avt
 
     # ---- CPU oracle on a bounded sample of the same workload -----------------------
     if not args.no_cpu_baseline:

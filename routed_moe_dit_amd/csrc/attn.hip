@@ -31,8 +31,9 @@
 // rounded to bf16: the k order of that MFMA is the accumulator's key order,
 // and vt's swapped positions give the V^T operand the same order.  K and V^T
 // tiles come from global memory straight into LDS (global_load_lds_dwordx4,
-// two stages, chunks XOR-swizzled per row), issued by waves 0-3 between their
-// score MFMAs.
+// three stages, chunks XOR-swizzled per row), issued by waves 0-3 between
+// their score MFMAs; waves 4-7 run half a tile behind waves 0-3 (see
+// attn_fwd_kernel).
 #include "lbv_internal.h"
 #include "lbv_pipe.h"
 
@@ -145,18 +146,29 @@ struct AttnArgs {
     int S, Sp, H, heads, B, nqt;
 };
 
-// LDS: two stages of [K tile: 64 rows x 256 bytes | V^T tile: 128 rows x 128
+// LDS: three stages of [K tile: 64 rows x 256 bytes | V^T tile: 128 rows x 128
 // bytes], then the sample's key mask, 64 keys per word.
 constexpr int KBYTES = KT * D * 2;               // 16 KB
 constexpr int VBYTES = D * KT * 2;               // 16 KB
 constexpr int STAGE_BYTES = KBYTES + VBYTES;
+constexpr int NSTG = 3;
 
+// Two wave groups share each SIMD (wave w and w + 4): group A (waves 0-3)
+// runs, between two barriers, the scores of tile j, their softmax and the PV
+// product of tile j; group B (waves 4-7) runs the softmax and PV product of
+// tile j - 1 and then the scores of tile j.  One barrier per tile holds the
+// groups half a tile apart, so on every SIMD one wave's softmax (vector ALU)
+// runs beside the other wave's matrix products.  Group A also issues the
+// copies of tile j + 1 (into the stage that held tile j - 2, which both groups
+// finished before the previous barrier) and waits for them before the
+// barrier; B reads tile j - 1's V^T and tile j's K, both landed.
 __global__ __launch_bounds__(NWV * 64) void attn_fwd_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds[NSTG * STAGE_BYTES];
     __shared__ unsigned long long kmask[MAXW];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool grpA = wave < 4;
     const int hl = lane >> 5, ql = lane & 31;
     // workgroups of one (sample, head) are consecutive in the logical order
     // and share an XCD (and its L2) for the K and V^T tiles
@@ -186,7 +198,7 @@ __global__ __launch_bounds__(NWV * 64) void attn_fwd_kernel(AttnArgs a) {
         for (int st = 0; st < D / 16; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qp + st * 16);
     }
 
-    // ---- copy sources (waves 0-3): K tile rows w*16 + 4i + lane/16, V^T rows
+    // ---- copy sources (group A): K tile rows w*16 + 4i + lane/16, V^T rows
     // w*32 + 8i + lane/8; lane lands at physical chunk lane%16 (K) or lane%8
     // (V^T), holding logical chunk c ^ swizzle(row) ------------------------------
     const char* kbase = reinterpret_cast<const char*>(a.k + tb * a.H + head * D);
@@ -213,7 +225,6 @@ __global__ __launch_bounds__(NWV * 64) void attn_fwd_kernel(AttnArgs a) {
         lds_dma16_sb<0>(vbase + kt * KT * 2, voff[i],
                         lds0 + stage * STAGE_BYTES + KBYTES + (wave & 3) * 4096 + i * 1024);
     };
-    const bool copier = wave < 4;
 
     // ---- fragment addresses ----------------------------------------------------
     // K (A operand of the score MFMA): key row 32 blk + ql, channels 16 st + 8 hl
@@ -233,26 +244,15 @@ __global__ __launch_bounds__(NWV * 64) void attn_fwd_kernel(AttnArgs a) {
     f32x16 oacc[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
+    f32x16 sacc[2];
     // running maximum (log2 domain, scaled) and this half-wave's running sum
     float mrun = -1e30f, lrun = 0.0f;
     const float csc = 1.4426950408889634f / sqrtf(static_cast<float>(D));   // log2(e) / sqrt(D)
 
-    // ---- prologue: tile 0 into stage 0 ----------------------------------------------
-    if (copier) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            copy_k(0, 0, i);
-            copy_v(0, 0, i);
-        }
-    }
-    wait_vmcnt<0>();
-    __syncthreads();                                  // mask words and stage 0 visible
-
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int stg = kt & 1;
-        const bool more = kt + 1 < nkt;
-        // ---- scores S^T = K Q^T; the copies of tile kt + 1 ride along --------------
-        f32x16 sacc[2];
+    // scores S^T = K Q^T of tile kt; group A also copies tile kt + 1
+    auto scores = [&](int kt, bool copy) {
+        const int stg = kt % NSTG;
+        const int cst = (kt + 1) % NSTG;
         bf16x8 kf0 = kfrag(stg, 0, 0), kf1 = kfrag(stg, 1, 0);
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
@@ -262,16 +262,21 @@ __global__ __launch_bounds__(NWV * 64) void attn_fwd_kernel(AttnArgs a) {
                 nk1 = kfrag(stg, 1, st + 1);
             }
             sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[st], st == 0 ? f32x16{} : sacc[0], 0, 0, 0);
-            if (copier && more && st < 4) copy_k(stg ^ 1, kt + 1, st);
+            if (copy && st < 4) copy_k(cst, kt + 1, st);
             sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf1, qf[st], st == 0 ? f32x16{} : sacc[1], 0, 0, 0);
-            if (copier && more && st < 4) copy_v(stg ^ 1, kt + 1, st);
+            if (copy && st < 4) copy_v(cst, kt + 1, st);
             __builtin_amdgcn_sched_barrier(0);
             if (st + 1 < D / 16) {
                 kf0 = nk0;
                 kf1 = nk1;
             }
         }
-        // ---- online softmax (exp2 domain), lazy rescale ---------------------------------
+    };
+
+    // online softmax of tile kt's scores (exp2 domain, lazy rescale), then
+    // O^T += V^T P^T
+    auto softmax_pv = [&](int kt) {
+        const int stg = kt % NSTG;
         const unsigned long long km = kmask[kt];
         if (km != ~0ull) {
 #pragma unroll
@@ -317,7 +322,6 @@ __global__ __launch_bounds__(NWV * 64) void attn_fwd_kernel(AttnArgs a) {
                 pf[blk * 2 + half] = __builtin_bit_cast(bf16x8, w);
             }
         lrun += psum;
-        // ---- O^T += V^T P^T -----------------------------------------------------------
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             bf16x8 vf[D / 32];
@@ -327,10 +331,40 @@ __global__ __launch_bounds__(NWV * 64) void attn_fwd_kernel(AttnArgs a) {
             for (int dblk = 0; dblk < D / 32; ++dblk)
                 oacc[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dblk], pf[c], oacc[dblk], 0, 0, 0);
         }
-        // tile kt + 1 landed; every wave done with stage stg
-        wait_vmcnt<0>();
+    };
+
+    // ---- prologue: tile 0 into stage 0 ----------------------------------------------
+    if (grpA) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            copy_k(0, 0, i);
+            copy_v(0, 0, i);
+        }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();                                  // mask words and stage 0 visible
+
+    // each group passes nkt barriers, one per tile (separate loops keep each
+    // group's registers to its own schedule)
+    if (grpA) {
+        for (int kt = 0; kt < nkt; ++kt) {
+            scores(kt, kt + 1 < nkt);
+            softmax_pv(kt);
+            wait_vmcnt<0>();                          // tile kt + 1 landed
+            wait_lgkmcnt0();
+            block_barrier();
+        }
+    } else {
+        scores(0, false);
         wait_lgkmcnt0();
         block_barrier();
+        for (int kt = 1; kt < nkt; ++kt) {
+            softmax_pv(kt - 1);
+            scores(kt, false);
+            wait_lgkmcnt0();
+            block_barrier();
+        }
+        softmax_pv(nkt - 1);
     }
 
     // ---- output: O = O^T / l; lane holds its query's channels 32 dblk + 8 j +
