@@ -197,22 +197,25 @@ def down_combine(wl, act_slots, ids, w, w2, shared_w2=None):
     return out
 
 
-def adaln_rmsnorm(x, temb6, table, eps=1e-6, round_bf16=True, per_token=True):
-    """h = rmsnorm(x) * (1 + scale) + shift (rows 4 and 3 of table + temb6),
-    fp64, rounded to bf16 when round_bf16.  x [n, H] fp32; temb6 [n, 6, H]
-    (per_token) or [6, H]; table [6, H].  Returns fp32 [n, H]."""
+def adaln_rmsnorm(x, temb6, table, eps=1e-6, round_bf16=True, per_token=True, rows=(3, 4)):
+    """h = rmsnorm(x) * (1 + scale) + shift, shift and scale the rows
+    rows = (shift, scale) of table + temb6 ((3, 4) in front of the FFN block,
+    (0, 1) in front of the attention block), fp64, rounded to bf16 when
+    round_bf16.  x [n, H] fp32; temb6 [n, 6, H] (per_token) or [6, H];
+    table [6, H].  Returns fp32 [n, H]."""
     x, temb6, table = _f32(x), _f32(temb6), _f32(table)
     n, H = x.shape
     assert table.shape == (6, H)
     assert temb6.shape == ((n, 6, H) if per_token else (6, H))
     h = np.empty((n, H), np.float32)
     L = lib()
-    L.orc_adaln_rmsnorm.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
-                                    ctypes.c_int64, ctypes.c_void_p, ctypes.c_double, ctypes.c_int,
-                                    ctypes.c_void_p]
-    L.orc_adaln_rmsnorm.restype = None
-    L.orc_adaln_rmsnorm(H, n, _p(x), _p(temb6), 6 * H if per_token else 0, _p(table), float(eps),
-                        int(bool(round_bf16)), _p(h))
+    L.orc_adaln_rmsnorm_rows.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                         ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_void_p]
+    L.orc_adaln_rmsnorm_rows.restype = None
+    L.orc_adaln_rmsnorm_rows(H, n, _p(x), _p(temb6), 6 * H if per_token else 0, _p(table),
+                             float(eps), int(bool(round_bf16)), int(rows[0]), int(rows[1]), _p(h))
     return h
 
 
@@ -364,6 +367,21 @@ def attn_forward(x, w_qkv, b_qkv, g_q, g_k, eps, cos, sin, heads, S, mask, w_o, 
     q, k, v = attn_qkv(x, w_qkv, b_qkv, g_q, g_k, eps, cos, sin, heads)
     o = bf16_round(attention(q, k, v, S, mask, qrows)).reshape(-1, H).astype(np.float32)
     return bf16_round(linear(o, w_o, b_o)).astype(np.float32)
+
+
+def attn_half_adaln(x, temb6, table, eps, w_qkv, b_qkv, g_q, g_k, qk_eps, cos, sin, heads, S,
+                    mask, w_o, b_o, qrows=None):
+    """The attention half of a DiT layer: h = AdaLN(x) with rows 0 (shift) and
+    1 (scale) of table + temb6 (bf16), the attention half on h (bf16 block
+    output), then out = x + gate * block with gate = row 2, fp64.  x [T, H]
+    fp32; temb6 [T, 6, H].  Returns [len(qrows) or T, H] float64."""
+    T, H = x.shape
+    h = adaln_rmsnorm(x, temb6, table, eps, True, True, rows=(0, 1))
+    blk = attn_forward(h, w_qkv, b_qkv, g_q, g_k, qk_eps, cos, sin, heads, S, mask, w_o, b_o,
+                       qrows=qrows).astype(np.float64)
+    rows = np.arange(T) if qrows is None else np.asarray(qrows)
+    gate = table[2].astype(np.float64)[None, :] + np.asarray(temb6, np.float64)[rows, 2]
+    return x[rows].astype(np.float64) + gate * blk
 
 
 def expert_act(wl, x_row, w13, e):

@@ -462,9 +462,11 @@ static double bf16_round_d(double d)
  * temb6 row t at temb6 + t * temb_stride (6 H fp32 values; stride 0: one row
  * for all tokens); table [6, H].
  */
-void orc_adaln_rmsnorm(int H, int64_t ntok, const float *x, const float *temb6,
-                       int64_t temb_stride, const float *table, double eps, int round_bf16,
-                       float *h)
+/* The same with the (shift, scale) rows given: 3, 4 in front of the FFN
+ * block, 0, 1 in front of the attention block of a layer. */
+void orc_adaln_rmsnorm_rows(int H, int64_t ntok, const float *x, const float *temb6,
+                            int64_t temb_stride, const float *table, double eps, int round_bf16,
+                            int shift_row, int scale_row, float *h)
 {
 #pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < ntok; ++t) {
@@ -474,12 +476,19 @@ void orc_adaln_rmsnorm(int H, int64_t ntok, const float *x, const float *temb6,
         for (int i = 0; i < H; ++i) ss += (double)xt[i] * (double)xt[i];
         const double r = 1.0 / sqrt(ss / H + eps);
         for (int i = 0; i < H; ++i) {
-            const double shift = (double)table[3 * H + i] + (double)et[3 * H + i];
-            const double scale = (double)table[4 * H + i] + (double)et[4 * H + i];
+            const double shift = (double)table[shift_row * H + i] + (double)et[shift_row * H + i];
+            const double scale = (double)table[scale_row * H + i] + (double)et[scale_row * H + i];
             const double v = (double)xt[i] * r * (1.0 + scale) + shift;
             h[t * H + i] = (float)(round_bf16 ? bf16_round_d(v) : v);
         }
     }
+}
+
+void orc_adaln_rmsnorm(int H, int64_t ntok, const float *x, const float *temb6,
+                       int64_t temb_stride, const float *table, double eps, int round_bf16,
+                       float *h)
+{
+    orc_adaln_rmsnorm_rows(H, ntok, x, temb6, temb_stride, table, eps, round_bf16, 3, 4, h);
 }
 
 /* The nearest bf16 value of each double (exposed for its pin). */

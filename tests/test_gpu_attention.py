@@ -272,3 +272,49 @@ def test_attn_samples_isolated_bitwise():
     inp1["mask"] = np.ascontiguousarray(inp["mask"][sl])
     got1 = run_forward(one, inp1)
     assert np.array_equal(got[sl], got1)
+
+
+def test_attn_forward_in_hip_graph_replays_bitwise():
+    """lbv_attn_forward only enqueues kernels on the caller's stream (its
+    set-up is a kernel, not a memset), so it can be captured in a HIP graph:
+    each replay, with a changed input and eager work in between, equals the
+    eager call bitwise."""
+    aw = synth.ATTN_WORKLOADS[1]
+    note("attn graph capture %s" % aw.name)
+    inp = synth.make_attn_inputs(aw)
+    cfg = lbv.attn_config(hidden=aw.hidden, num_heads=aw.heads, eps=1e-6)
+    T, H = aw.T, aw.hidden
+    x0 = bf16(inp["x"])
+    x = x0.clone()
+    dd = {k: f32(inp[k]) for k in ("b_qkv", "g_q", "g_k", "cos", "sin", "b_o")}
+    w_qkv, w_o, mask = bf16(inp["w_qkv"]), bf16(inp["w_o"]), u8(inp["mask"])
+    out = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(lbv.lbv_attn_workspace_size(cfg, aw.B, aw.S), dtype=torch.uint8,
+                     device="cuda")
+
+    def call():
+        lbv.lbv_attn_forward(cfg, aw.B, aw.S, x, mask, w_qkv, dd["b_qkv"], dd["g_q"], dd["g_k"],
+                             dd["cos"], dd["sin"], w_o, dd["b_o"], out, ws,
+                             torch.cuda.current_stream())
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    for rep in range(3):
+        if rep:
+            x.copy_(x0[torch.randperm(T, generator=gen).cuda()])
+        torch.cuda.synchronize()
+        call()
+        torch.cuda.synchronize()
+        ref = out.clone()
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), rep

@@ -178,3 +178,49 @@ def test_forward_fp8_matches_bf16_block_on_dequantized_weights():
     m = metrics(host(out8), host(out16))
     print("fp8 block vs bf16 block on dequantized weights: %s" % m)
     assert m["rel_frob"] <= 5e-3 and m["max_abs"] <= 3e-2
+
+
+def test_forward_fp8_in_hip_graph_replays_bitwise():
+    """lbv_moe_forward_fp8 only enqueues kernels on the caller's stream, so it
+    can be captured in a HIP graph: each replay, with a changed input and eager
+    work in between, equals the eager call bitwise."""
+    wl = W[2]
+    note("fp8 graph capture %s" % wl.name)
+    inp = synth.make_inputs(wl)
+    d = upload(wl, inp)
+    cfg = cfg_for(wl)
+    wq = lbv.quantize_fp8_weights(d["w13"], d["w2"], d["shared_w13"], d["shared_w2"])
+    T = d["x"].shape[0]
+    x = d["x"].clone()
+    out = torch.empty_like(x)
+    ids = torch.empty(T, wl.top_k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, wl.top_k, dtype=torch.float32, device="cuda")
+    ws = torch.empty(lbv.lbv_moe_workspace_size(cfg, T), dtype=torch.uint8, device="cuda")
+
+    def call():
+        lbv.lbv_moe_forward_fp8(cfg, x, d["mask"], d["router_w"], d["e_bias"], wq, out, ids, w,
+                                ws, torch.cuda.current_stream())
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    gen = torch.Generator(device="cpu").manual_seed(6)
+    for rep in range(3):
+        if rep:
+            x.copy_(d["x"][torch.randperm(T, generator=gen).cuda()])
+        torch.cuda.synchronize()
+        call()
+        torch.cuda.synchronize()
+        ref = (out.clone(), ids.clone(), w.clone())
+        out.zero_()
+        ids.zero_()
+        w.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]) and torch.equal(ids, ref[1]) and torch.equal(w, ref[2]), rep

@@ -141,3 +141,21 @@ def test_gated_residual():
     # the block sees h, and the router's ids come from h
     blk = oracle.moe_forward(wl, r1["h"], *args)
     assert np.array_equal(blk["ids"], r1["block"]["ids"])
+
+
+def test_modulation_rows_are_selectable():
+    """Rows (shift, scale): (3, 4) in front of the FFN block (the default),
+    (0, 1) in front of the attention block.  With eps = 0 a constant row a
+    normalises to sign(a), so h = sign(a) (1 + scale) + shift exactly."""
+    H = 64
+    table = np.repeat((0.1 * (np.arange(6) + 1))[:, None], H, 1).astype(np.float32)
+    temb6 = np.zeros((2, 6, H), np.float32)
+    x = np.stack([np.full(H, 3.0), np.full(H, -0.5)]).astype(np.float32)
+    sgn = np.array([1.0, -1.0])[:, None]
+    for rows, (sh, sc) in (((3, 4), (0.4, 0.5)), ((0, 1), (0.1, 0.2))):
+        h = oracle.adaln_rmsnorm(x, temb6, table, 0.0, round_bf16=False, rows=rows)
+        want = sgn * (1 + np.float64(np.float32(sc))) + np.float64(np.float32(sh))
+        assert np.allclose(h, np.broadcast_to(want, (2, H)), rtol=1e-7), rows
+    assert np.array_equal(oracle.adaln_rmsnorm(x, temb6, table, 0.0, round_bf16=False),
+                          oracle.adaln_rmsnorm(x, temb6, table, 0.0, round_bf16=False,
+                                               rows=(3, 4)))

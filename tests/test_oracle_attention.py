@@ -234,3 +234,43 @@ def test_qkv_blocks_and_norm_weights():
         want = oracle.bf16_round(np.sign(c) * g.astype(np.float64) / np.sqrt(1 + 1e-6 / c ** 2))
         assert np.array_equal(got, np.broadcast_to(want, (T, heads, D)).astype(np.float32))
     assert (v == 0.25).all()
+
+
+def test_attention_half_with_adaln_closed_form():
+    """The attention half of a layer: h = AdaLN(x) with rows 0 (shift) and
+    1 (scale), the half on h, out = x + gate * block with gate = row 2.  With
+    zero q/k projections every valid key weighs the same, so block =
+    bf16(bf16(mean of the sample's valid h) W_o^T + b_o) and the output is
+    x + (table[2] + temb6[t, 2]) block, in closed form."""
+    T, S, H, heads = 12, 6, 32, 2
+    r = rng(8)
+    x = r.standard_normal((T, H)).astype(np.float32)
+    table = (r.standard_normal((6, H)) * 0.3).astype(np.float32)
+    temb6 = (r.standard_normal((T, 6, H)) * 0.3).astype(np.float32)
+    w_qkv = np.zeros((3 * H, H), np.float32)
+    w_qkv[2 * H:] = np.eye(H, dtype=np.float32)
+    b_qkv = np.zeros(3 * H, np.float32)
+    g = np.ones(H // heads, np.float32)
+    cos, sin, _ = tables(np.arange(T) * 1.0, H // heads)
+    mask = np.ones(T, np.uint8)
+    mask[[5, 11]] = 0
+    w_o = oracle.bf16_round(r.standard_normal((H, H)) * 0.1).astype(np.float32)
+    b_o = (r.standard_normal(H) * 0.1).astype(np.float32)
+    out = oracle.attn_half_adaln(x, temb6, table, 1e-6, w_qkv, b_qkv, g, g, 1e-6, cos, sin, heads,
+                                 S, mask, w_o, b_o)
+    # h from its own closed form: rmsnorm(x) (1 + scale row 1) + shift row 0, bf16
+    xd = x.astype(np.float64)
+    rn = xd / np.sqrt((xd * xd).mean(1, keepdims=True) + 1e-6)
+    t64 = table.astype(np.float64)
+    e64 = temb6.astype(np.float64)
+    h = oracle.bf16_round(rn * (1 + t64[1] + e64[:, 1]) + t64[0] + e64[:, 0])
+    for b in range(2):
+        rows = [t for t in range(b * S, (b + 1) * S) if mask[t]]
+        blk = oracle.bf16_round(oracle.bf16_round(h[rows].mean(0)) @ w_o.astype(np.float64).T + b_o)
+        for t in range(b * S, (b + 1) * S):
+            bt = blk if mask[t] else oracle.bf16_round(b_o.astype(np.float64))
+            want = xd[t] + (t64[2] + e64[t, 2]) * bt
+            assert np.allclose(out[t], want, rtol=1e-12, atol=1e-12), t
+    sub = oracle.attn_half_adaln(x, temb6, table, 1e-6, w_qkv, b_qkv, g, g, 1e-6, cos, sin, heads,
+                                 S, mask, w_o, b_o, qrows=[7, 2])
+    assert np.array_equal(sub, out[[7, 2]])
