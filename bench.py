@@ -414,6 +414,20 @@ def main():
                                                         stream),
             }
             part_ms = {k_: float(np.median(timed_n(f_, nrep))) for k_, f_ in parts.items()}
+            # the same half with its AdaLN (rows 0, 1) and gated residual (row 2)
+            ada = synth.make_attn_adaln_inputs(aw)
+            xr = torch.from_numpy(ada["x"]).cuda()
+            temb = torch.from_numpy(ada["temb6"]).cuda()
+            table = torch.from_numpy(ada["table"]).cuda()
+            del ada
+            hout = torch.empty_like(xr)
+            hws = torch.empty(lbv.lbv_attn_half_adaln_workspace_size(acfg, B_, S_),
+                              dtype=torch.uint8, device="cuda")
+            ha_ms = timed_n(lambda: lbv.lbv_attn_half_adaln(
+                acfg, B_, S_, xr, ad["mask"], temb, table, 1e-6, ad["w_qkv"], ad["b_qkv"],
+                ad["g_q"], ad["g_k"], ad["cos"], ad["sin"], ad["w_o"], ad["b_o"], hout, hws,
+                stream), nrep)
+            del xr, temb, table, hout, hws
             valid = [min(v_, S_) for v_ in aw.valid]
             attn_flops = 4.0 * sum(v_ * v_ for v_ in valid) * H      # QK^T and PV, valid tokens
             a_s = part_ms["attention"] * 1e-3
@@ -421,6 +435,7 @@ def main():
                 "workload": aw.name,
                 "ms": float(np.median(h_ms)),
                 "tokens_per_s": T / (float(np.median(h_ms)) * 1e-3),
+                "with_adaln_and_residual_ms": float(np.median(ha_ms)),
                 "stage_ms": part_ms,
                 "qkv_proj_tflops": 2.0 * T * 3 * H * H / (part_ms["qkv_proj"] * 1e-3) / 1e12,
                 "out_proj_tflops": 2.0 * T * H * H / (part_ms["out_proj"] * 1e-3) / 1e12,

@@ -96,7 +96,7 @@ typedef struct {
 
 /* Version of this ABI (bumped on any signature or layout change; 2: the
  * gate/up call takes a workspace; 3: fp8 expert weights; 4: the attention
- * half). */
+ * half; 5: the attention half with its AdaLN and gated residual). */
 int32_t lbv_abi_version(void);
 
 /* Human-readable name of a status code (static storage). */
@@ -424,6 +424,31 @@ lbv_status lbv_attn_forward(const lbv_attn_config *cfg, int64_t B, int64_t S, co
                             const float *g_q, const float *g_k, const float *cos_t,
                             const float *sin_t, const void *w_o, const float *b_o, void *out,
                             void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace of lbv_attn_half_adaln: lbv_attn_workspace_size plus h and the
+ * block output, [B S, H] bf16 each. */
+lbv_status lbv_attn_half_adaln_workspace_size(const lbv_attn_config *cfg, int64_t B, int64_t S,
+                                              size_t *bytes);
+
+/*
+ * The attention half of a DiT layer with its modulation (prhub summary of
+ * sglang PR #32341, "实现拆解" step 2; the same reading as the FFN half's,
+ * with the first three rows): h = rmsnorm(x) * (1 + scale) + shift with
+ * (shift, scale, gate) = rows 0, 1, 2 of table + temb6 row t (fp32), h
+ * rounded to bf16; the attention half on h (lbv_attn_forward, bf16 block
+ * output); out[t] = x[t] + gate[t] * block[t] in fp32.  x, out [B S, H] fp32
+ * (out may be x itself, but may not overlap it otherwise); temb6 / table /
+ * eps as for lbv_adaln_rmsnorm (eps of this norm; cfg->eps is the q/k head
+ * norms'); the attention operands as for lbv_attn_forward; ws:
+ * lbv_attn_half_adaln_workspace_size bytes.
+ */
+lbv_status lbv_attn_half_adaln(const lbv_attn_config *cfg, int64_t B, int64_t S, const float *x,
+                               const uint8_t *mask, const float *temb6, int64_t temb_stride,
+                               const float *table, float eps, const void *w_qkv,
+                               const float *b_qkv, const float *g_q, const float *g_k,
+                               const float *cos_t, const float *sin_t, const void *w_o,
+                               const float *b_o, float *out, void *ws, size_t ws_bytes,
+                               hipStream_t stream);
 
 #ifdef __cplusplus
 }

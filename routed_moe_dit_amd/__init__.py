@@ -25,7 +25,8 @@ __all__ = [
     "lbv_moe_ffn_adaln_workspace_size", "lbv_moe_ffn_adaln", "Fp8Weights",
     "lbv_quantize_fp8_rows", "quantize_fp8_weights", "lbv_moe_forward_fp8", "AttnConfig",
     "attn_config", "attn_sp", "lbv_attn_workspace_size", "lbv_linear_bf16", "lbv_attn_qk_prep",
-    "lbv_attn_core", "lbv_attn_forward", "EXPORTS", "LIB_PATH",
+    "lbv_attn_core", "lbv_attn_forward", "lbv_attn_half_adaln_workspace_size",
+    "lbv_attn_half_adaln", "EXPORTS", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblbv_moe.so")
@@ -44,7 +45,8 @@ EXPORTS = (
     "lbv_moe_permute", "lbv_moe_gemm_w13_silu", "lbv_moe_gemm_w2_combine", "lbv_moe_forward",
     "lbv_adaln_rmsnorm", "lbv_moe_ffn_adaln_workspace_size", "lbv_moe_ffn_adaln",
     "lbv_quantize_fp8_rows", "lbv_moe_forward_fp8", "lbv_attn_workspace_size", "lbv_linear_bf16",
-    "lbv_attn_qk_prep", "lbv_attn_core", "lbv_attn_forward",
+    "lbv_attn_qk_prep", "lbv_attn_core", "lbv_attn_forward", "lbv_attn_half_adaln_workspace_size",
+    "lbv_attn_half_adaln",
 )
 
 
@@ -172,6 +174,11 @@ def load():
     L.lbv_attn_core.restype = st
     L.lbv_attn_forward.argtypes = [A, I64, I64, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     L.lbv_attn_forward.restype = st
+    L.lbv_attn_half_adaln_workspace_size.argtypes = [A, I64, I64, ctypes.POINTER(SZ)]
+    L.lbv_attn_half_adaln_workspace_size.restype = st
+    L.lbv_attn_half_adaln.argtypes = [A, I64, I64, P, P, P, I64, P, F, P, P, P, P, P, P, P, P, P,
+                                      P, SZ, P]
+    L.lbv_attn_half_adaln.restype = st
     _lib = L
     return L
 
@@ -641,6 +648,37 @@ def lbv_attn_forward(cfg, B, S, x, mask, w_qkv, b_qkv, g_q, g_k, cos, sin, w_o, 
         _ptr(g_k, "g_k", f), _ptr(cos, "cos", f), _ptr(sin, "sin", f), _ptr(w_o, "w_o", bf),
         _ptr(b_o, "b_o", f), _ptr(out, "out", bf), _ptr(ws, "ws"),
         ws.numel() * ws.element_size(), _stream(stream)), "lbv_attn_forward")
+
+
+def lbv_attn_half_adaln_workspace_size(cfg: AttnConfig, B: int, S: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().lbv_attn_half_adaln_workspace_size(ctypes.byref(cfg), B, S, ctypes.byref(n)),
+           "lbv_attn_half_adaln_workspace_size")
+    return n.value
+
+
+def lbv_attn_half_adaln(cfg, B, S, x, mask, temb6, table, eps, w_qkv, b_qkv, g_q, g_k, cos, sin,
+                        w_o, b_o, out, ws, stream=None):
+    """The attention half with AdaLN (rows 0, 1) and the gated residual
+    (row 2): x, out [B S, H] fp32; temb6 [B S, 6, H] or [6, H] (shared)."""
+    H = cfg.hidden
+    T = B * S
+    _attn_shapes(cfg, B, S, mask=mask, w_qkv=w_qkv, b_qkv=b_qkv, g_q=g_q, g_k=g_k, cos=cos,
+                 sin=sin, w_o=w_o, b_o=b_o)
+    _shape(x, "x", T, H)
+    _shape(out, "out", T, H)
+    _shape(table, "table", 6, H)
+    stride = _temb_rows(temb6, T, H)
+    _need(ws, "ws")
+    _same_device(x, mask, temb6, table, w_qkv, b_qkv, g_q, g_k, cos, sin, w_o, b_o, out, ws)
+    bf, f = torch.bfloat16, torch.float32
+    _check(load().lbv_attn_half_adaln(
+        ctypes.byref(cfg), B, S, _ptr(x, "x", f), _ptr(mask, "mask", torch.uint8),
+        _ptr(temb6, "temb6", f), stride, _ptr(table, "table", f), float(eps),
+        _ptr(w_qkv, "w_qkv", bf), _ptr(b_qkv, "b_qkv", f), _ptr(g_q, "g_q", f),
+        _ptr(g_k, "g_k", f), _ptr(cos, "cos", f), _ptr(sin, "sin", f), _ptr(w_o, "w_o", bf),
+        _ptr(b_o, "b_o", f), _ptr(out, "out", f), _ptr(ws, "ws"), ws.numel() * ws.element_size(),
+        _stream(stream)), "lbv_attn_half_adaln")
 
 
 class MoEBlock:

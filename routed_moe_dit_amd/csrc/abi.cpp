@@ -13,7 +13,7 @@ using lbv::Dims;
 
 namespace {
 
-constexpr int32_t kAbiVersion = 4;
+constexpr int32_t kAbiVersion = 5;
 constexpr size_t kAlign = 256;
 
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -597,6 +597,67 @@ lbv_status lbv_attn_core(const lbv_attn_config* cfg, int64_t B, int64_t S, const
     if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o)) return LBV_ERR_ALIGN;
     return hip_status(lbv::launch_attn_core(static_cast<int>(B), static_cast<int>(S), cfg->hidden,
                                             cfg->num_heads, q, k, vt, mask, o, stream));
+}
+
+lbv_status lbv_attn_half_adaln_workspace_size(const lbv_attn_config* cfg, int64_t B, int64_t S,
+                                              size_t* bytes) {
+    if (!bytes) return LBV_ERR_NULL;
+    lbv_status st = check_attn(cfg, B, S);
+    if (st != LBV_OK) return st;
+    const size_t hb = round_up(static_cast<size_t>(B * S) * cfg->hidden * 2);
+    *bytes = attn_layout(cfg, B, S).total + 2 * hb;
+    return LBV_OK;
+}
+
+lbv_status lbv_attn_half_adaln(const lbv_attn_config* cfg, int64_t B, int64_t S, const float* x,
+                               const uint8_t* mask, const float* temb6, int64_t temb_stride,
+                               const float* table, float eps, const void* w_qkv,
+                               const float* b_qkv, const float* g_q, const float* g_k,
+                               const float* cos_t, const float* sin_t, const void* w_o,
+                               const float* b_o, float* out, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+    lbv_status st = check_attn(cfg, B, S);
+    if (st != LBV_OK) return st;
+    if (B == 0 || S == 0) return LBV_OK;
+    if (!x || !temb6 || !table || !w_qkv || !g_q || !g_k || !cos_t || !sin_t || !w_o || !out ||
+        !ws)
+        return LBV_ERR_NULL;
+    if (!aligned16(x) || !aligned16(temb6) || !aligned16(table) || !aligned16(out) ||
+        !aligned16(w_qkv) || !aligned16(w_o) || !aligned16(ws) || !aligned4(b_qkv) ||
+        !aligned4(b_o) || !aligned4(g_q) || !aligned4(g_k) || !aligned4(cos_t) || !aligned4(sin_t))
+        return LBV_ERR_ALIGN;
+    if (temb_stride < 0 || temb_stride % 4 != 0) return LBV_ERR_ALIGN;
+    if (!(eps >= 0.0f) || !isfinite(eps)) return LBV_ERR_SHAPE;
+    const AttnLayout L = attn_layout(cfg, B, S);
+    const int64_t T = B * S;
+    const int H = cfg->hidden;
+    const size_t hb = round_up(static_cast<size_t>(T) * H * 2);
+    if (ws_bytes < L.total + 2 * hb) return LBV_ERR_WORKSPACE;
+    const size_t xb = static_cast<size_t>(T) * H * 4;
+    // in place (out == x) is allowed: each element is read, then written, by one lane
+    if (out != x && overlaps(x, xb, out, xb)) return LBV_ERR_ALIAS;
+    if (overlaps(ws, ws_bytes, out, xb) || overlaps(ws, ws_bytes, x, xb)) return LBV_ERR_ALIAS;
+    char* base = static_cast<char*>(ws);
+    void* h = base + L.total;
+    void* blk = base + L.total + hb;
+    lbv::AdalnArgs a{x, temb6, temb_stride, table, eps, h, T, H, stream};
+    a.shift_row = 0;
+    a.scale_row = 1;
+    hipError_t e = lbv::launch_adaln_bf16(a);
+    if (e == hipSuccess)
+        e = lbv::launch_linear(T, 3 * H, H, h, w_qkv, b_qkv, base + L.qkv, base + L.lin, stream);
+    if (e == hipSuccess)
+        e = lbv::launch_attn_prep(static_cast<int>(B), static_cast<int>(S), H, cfg->num_heads,
+                                  base + L.qkv, g_q, g_k, cos_t, sin_t, cfg->eps, base + L.q,
+                                  base + L.k, base + L.vt, stream);
+    if (e == hipSuccess)
+        e = lbv::launch_attn_core(static_cast<int>(B), static_cast<int>(S), H, cfg->num_heads,
+                                  base + L.q, base + L.k, base + L.vt, mask, base + L.o, stream);
+    if (e == hipSuccess)
+        e = lbv::launch_linear(T, H, H, base + L.o, w_o, b_o, blk, base + L.lin, stream);
+    if (e == hipSuccess)
+        e = lbv::launch_gated_residual(T, H, x, blk, temb6, temb_stride, table, 2, out, stream);
+    return hip_status(e);
 }
 
 lbv_status lbv_attn_forward(const lbv_attn_config* cfg, int64_t B, int64_t S, const void* x,

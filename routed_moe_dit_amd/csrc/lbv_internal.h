@@ -120,8 +120,17 @@ struct AdalnArgs {
     int64_t T;
     int H;
     hipStream_t stream;
+    int shift_row = 3;     // rows of table / temb6: 3, 4 in front of the FFN
+    int scale_row = 4;     // block, 0, 1 in front of the attention block
 };
 hipError_t launch_adaln(const Dims& d, const AdalnArgs& a);
+hipError_t launch_adaln_bf16(const AdalnArgs& a);
+
+// out[t] = x[t] + (table[row] + temb row t [row]) * y[t], y bf16, fp32 in and
+// out (out may be x)
+hipError_t launch_gated_residual(int64_t T, int H, const float* x, const void* y,
+                                 const float* temb, int64_t temb_stride, const float* table,
+                                 int row, float* out, hipStream_t stream);
 
 // combine + gated residual: out[t] = x[t] + gate[t] * (sum_k w y + shared y),
 // gate = table[5] + temb6 row t [5], fp32 in and out (out may be x)

@@ -35,7 +35,7 @@ __all__ = [
     "Workload", "WORKLOADS", "by_name", "make_inputs", "round_to_bf16",
     "bf16_bits", "bits_to_f32", "digest", "token_mask", "random_act", "make_adaln_inputs",
     "AttnWorkload", "ATTN_WORKLOADS", "attn_by_name", "make_attn_inputs", "joint_positions",
-    "rope_tables",
+    "rope_tables", "make_attn_adaln_inputs",
 ]
 
 
@@ -350,3 +350,15 @@ def make_attn_inputs(aw: AttnWorkload) -> dict:
             mask[b * aw.S:b * aw.S + v] = 1
     return dict(x=x, w_qkv=w_qkv, b_qkv=b_qkv, g_q=g_q, g_k=g_k, w_o=w_o, b_o=b_o, cos=cos,
                 sin=sin, mask=mask)
+
+
+def make_attn_adaln_inputs(aw: AttnWorkload, x_std: float = 1.0, table_std: float = 0.1,
+                           temb_std: float = 0.1) -> dict:
+    """The residual stream and modulation around the attention half (a stream
+    of its own, seed + 1000): ``x [T, H]``, ``table [6, H]`` and a token-level
+    ``temb6 [T, 6, H]``, float32 N(0, std^2)."""
+    rng = np.random.default_rng(aw.seed + 1000)
+    x = _draw(rng, (aw.T, aw.hidden), x_std)
+    table = _draw(rng, (6, aw.hidden), table_std)
+    temb6 = _draw(rng, (aw.T, 6, aw.hidden), temb_std)
+    return dict(x=x, table=table, temb6=temb6)

@@ -21,7 +21,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 24, names
+    assert len(names) == 26, names
     assert set(names) == set(lbv.EXPORTS)
     L = ctypes.CDLL(lbv.LIB_PATH)
     for n in names:
@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert lbv.lbv_abi_version() == 4
+    assert lbv.lbv_abi_version() == 5
     texts = {lbv.lbv_status_string(s) for s in range(9)}
     assert len(texts) == 9
     assert lbv.lbv_status_string(99) == "unknown status"
@@ -436,3 +436,21 @@ def test_attention_validation_paths():
     assert L.lbv_attn_core(ctypes.byref(c), 1, 8, A, B, None, None, Cc, None) == lbv.LBV_ERR_NULL
     assert L.lbv_attn_qk_prep(ctypes.byref(c), 1, 8, A, A, A, A, A, B, Cc, BIG + 8, None) == \
         lbv.LBV_ERR_ALIGN
+
+
+def test_attention_half_adaln_validation_paths():
+    L = raw()
+    c = lbv.attn_config()
+    T, H = 1600, 2048
+    need = lbv.lbv_attn_half_adaln_workspace_size(c, 2, 800)
+    assert need == lbv.lbv_attn_workspace_size(c, 2, 800) + 2 * T * H * 2
+
+    def f(x=A, out=Cc, temb_stride=6 * H, eps=1e-6, ws_bytes=need, B_=2):
+        return L.lbv_attn_half_adaln(ctypes.byref(c), B_, 800, x, None, B, temb_stride, B, eps, B,
+                                     None, A, A, A, A, B, None, out, BIG, ws_bytes, None)
+    assert f(B_=0) == lbv.LBV_OK
+    assert f(x=None) == lbv.LBV_ERR_NULL
+    assert f(temb_stride=6 * H + 2) == lbv.LBV_ERR_ALIGN
+    assert f(eps=-1.0) == lbv.LBV_ERR_SHAPE
+    assert f(ws_bytes=need - 1) == lbv.LBV_ERR_WORKSPACE
+    assert f(out=A + 4096) == lbv.LBV_ERR_ALIAS        # overlaps x without being x

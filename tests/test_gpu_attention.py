@@ -318,3 +318,81 @@ def test_attn_forward_in_hip_graph_replays_bitwise():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref), rep
+
+
+
+# ---- the attention half with its AdaLN and gated residual ----------------------------
+
+def run_half_adaln(aw, inp, ada, temb_shared=False):
+    cfg = lbv.attn_config(hidden=aw.hidden, num_heads=aw.heads, eps=1e-6)
+    T, H = aw.T, aw.hidden
+    out = torch.zeros(T, H, dtype=torch.float32, device="cuda")
+    ws = torch.empty(lbv.lbv_attn_half_adaln_workspace_size(cfg, aw.B, aw.S), dtype=torch.uint8,
+                     device="cuda")
+    temb = f32(ada["temb6"][0] if temb_shared else ada["temb6"])
+    lbv.lbv_attn_half_adaln(cfg, aw.B, aw.S, f32(ada["x"]), u8(inp["mask"]), temb,
+                            f32(ada["table"]), 1e-6, bf16(inp["w_qkv"]), f32(inp["b_qkv"]),
+                            f32(inp["g_q"]), f32(inp["g_k"]), f32(inp["cos"]), f32(inp["sin"]),
+                            bf16(inp["w_o"]), f32(inp["b_o"]), out, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def oracle_half_adaln(aw, inp, ada, rows=None, temb6=None):
+    return oracle.attn_half_adaln(ada["x"], ada["temb6"] if temb6 is None else temb6,
+                                  ada["table"], 1e-6, inp["w_qkv"], inp["b_qkv"], inp["g_q"],
+                                  inp["g_k"], 1e-6, inp["cos"], inp["sin"], aw.heads, aw.S,
+                                  inp["mask"], inp["w_o"], inp["b_o"], qrows=rows)
+
+
+def check_half(got, want, x, name):
+    """The residual is fp32 (x + gate * block): compare the update
+    gate * block, whose bf16 block carries the attention half's tolerance."""
+    check(got - x, want - x, name)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("aw", FWD_CASES, ids=lambda a: a.name)
+def test_attn_half_adaln_parity(aw):
+    note("attn half + adaln %s" % aw.name)
+    inp = synth.make_attn_inputs(aw)
+    ada = synth.make_attn_adaln_inputs(aw)
+    got = run_half_adaln(aw, inp, ada)
+    x = ada["x"].astype(np.float64)
+    check_half(got, oracle_half_adaln(aw, inp, ada), x, "attn half + adaln %s (every token)" % aw.name)
+
+
+def test_attn_half_adaln_shared_temb_and_in_place():
+    """A shared temb6 row (stride 0) and out == x."""
+    aw = FWD_CASES[1]
+    note("attn half + adaln shared temb, in place %s" % aw.name)
+    inp = synth.make_attn_inputs(aw)
+    ada = synth.make_attn_adaln_inputs(aw)
+    cfg = lbv.attn_config(hidden=aw.hidden, num_heads=aw.heads, eps=1e-6)
+    T, H = aw.T, aw.hidden
+    xo = f32(ada["x"])
+    ws = torch.empty(lbv.lbv_attn_half_adaln_workspace_size(cfg, aw.B, aw.S), dtype=torch.uint8,
+                     device="cuda")
+    lbv.lbv_attn_half_adaln(cfg, aw.B, aw.S, xo, u8(inp["mask"]), f32(ada["temb6"][0]),
+                            f32(ada["table"]), 1e-6, bf16(inp["w_qkv"]), f32(inp["b_qkv"]),
+                            f32(inp["g_q"]), f32(inp["g_k"]), f32(inp["cos"]), f32(inp["sin"]),
+                            bf16(inp["w_o"]), f32(inp["b_o"]), xo, ws)
+    torch.cuda.synchronize()
+    shared = np.broadcast_to(ada["temb6"][0], ada["temb6"].shape).copy()
+    want = oracle_half_adaln(aw, inp, ada, temb6=shared)
+    x = ada["x"].astype(np.float64)
+    check_half(xo.cpu().numpy().astype(np.float64), want, x, "attn half + adaln shared/in place")
+
+
+@pytest.mark.timeout(900)
+def test_attn_half_adaln_parity_full_size():
+    aw = synth.ATTN_WORKLOADS[2]
+    note("attn half + adaln full %s" % aw.name)
+    inp = synth.make_attn_inputs(aw)
+    ada = synth.make_attn_adaln_inputs(aw)
+    got = run_half_adaln(aw, inp, ada)
+    r = np.random.default_rng(1)
+    rows = np.unique(np.r_[0, aw.S - 1, aw.S, aw.T - 1, r.integers(0, aw.T, 196)])
+    x = ada["x"].astype(np.float64)[rows]
+    check_half(got[rows], oracle_half_adaln(aw, inp, ada, rows), x,
+               "attn half + adaln full (%d rows)" % len(rows))
