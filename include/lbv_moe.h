@@ -267,7 +267,8 @@ lbv_status lbv_moe_forward(const lbv_moe_config *cfg, int64_t T, const void *x,
 /*
  * Quantizes `rows` rows of `cols` weights (dtype LBV_BF16 or LBV_F32, finite
  * values) into q [rows, cols] e4m3fn codes and scale [rows] fp32 powers of
- * two.  cols must be a positive multiple of 16; w, q 16-byte aligned, scale
+ * two.  cols must be a positive multiple of 16, rows below 2^32 and
+ * rows * cols at most 2^40; w, q 16-byte aligned, scale
  * 4-byte aligned; q and scale must not overlap w.  rows == 0 is a no-op.
  * Expert weights quantize as [E * 2I, H] (w13), [E * H, I] (w2),
  * [2 I_s, H] (shared_w13) and [H, I_s] (shared_w2).

@@ -391,7 +391,8 @@ lbv_status lbv_quantize_fp8_rows(const void* w, int32_t dtype, int64_t rows, int
                                  uint8_t* q, float* scale, hipStream_t stream) {
     if (dtype != LBV_BF16 && dtype != LBV_F32) return LBV_ERR_UNSUPPORTED;
     if (rows < 0 || cols <= 0 || cols % 16 != 0 || cols > (1 << 30)) return LBV_ERR_SHAPE;
-    if (rows > (int64_t(1) << 40) / cols) return LBV_ERR_SHAPE;
+    // one wave per row, four rows per workgroup: the grid stays below 2^30
+    if (rows >= (int64_t(1) << 32) || rows > (int64_t(1) << 40) / cols) return LBV_ERR_SHAPE;
     if (rows == 0) return LBV_OK;
     if (!w || !q || !scale) return LBV_ERR_NULL;
     if (!aligned16(w) || !aligned16(q) || !aligned4(scale)) return LBV_ERR_ALIGN;

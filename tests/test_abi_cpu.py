@@ -361,6 +361,7 @@ def test_fp8_validation_paths():
     assert q(A, lbv.LBV_BF16, 4, 24, B, Cc, None) == lbv.LBV_ERR_SHAPE    # cols % 16
     assert q(A, lbv.LBV_BF16, 4, 0, B, Cc, None) == lbv.LBV_ERR_SHAPE
     assert q(A, lbv.LBV_BF16, -1, 64, B, Cc, None) == lbv.LBV_ERR_SHAPE
+    assert q(A, lbv.LBV_BF16, 1 << 32, 16, B, Cc, None) == lbv.LBV_ERR_SHAPE   # grid bound
     assert q(None, lbv.LBV_BF16, 0, 64, None, None, None) == lbv.LBV_OK   # no rows
     assert q(A, lbv.LBV_BF16, 4, 64, None, Cc, None) == lbv.LBV_ERR_NULL
     assert q(A, lbv.LBV_BF16, 4, 64, B + 8, Cc, None) == lbv.LBV_ERR_ALIGN
