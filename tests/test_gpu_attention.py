@@ -11,8 +11,11 @@ Bars:
   of them differ at all;
   vt is pure data movement and must match exactly;
 * attention and the whole half: relative Frobenius error 5e-3 and max-abs
-  3e-2 of the bf16 outputs (bf16 P in the PV product, fp32 accumulation),
-  every token (full size: sampled query rows, all keys).
+  3e-2 of the bf16 outputs (bf16 P in the PV product, fp32 accumulation)
+  before their final bf16 rounding, so an element may differ by one more
+  bf16 ulp of its magnitude; every token (full size: sampled query rows, all
+  keys).  The residual updates of the attention half with its modulation are
+  fp32 and held to 3e-2 with no such allowance.
 """
 import numpy as np
 import pytest
@@ -47,11 +50,20 @@ def bf16(a):
     return dev(np.ascontiguousarray(a, np.float32), "bf16")
 
 
-def check(got, want, name):
+def check(got, want, name, rounded=True):
+    """rounded: got and want are bf16 roundings of values that the bar holds
+    within TOL["max_abs"] of each other; each rounding moves a value by at
+    most half a bf16 ulp, so an element may differ by one ulp of its
+    magnitude beyond that (one ulp is 2^-5 from |o| = 4 on, above 3e-2)."""
     m = metrics(got, want)
+    d = np.abs(np.asarray(got, np.float64) - want)
+    if rounded and d.size:
+        m["max_abs_beyond_ulp"] = float(
+            np.maximum(d - ulp_bf16(np.maximum(np.abs(got), np.abs(want))), 0).max())
     print("%s: %s" % (name, m))
     assert m["finite"]
-    assert m["rel_frob"] <= TOL["rel_frob"] and m["max_abs"] <= TOL["max_abs"], m
+    assert m["rel_frob"] <= TOL["rel_frob"], m
+    assert m.get("max_abs_beyond_ulp", m["max_abs"]) <= TOL["max_abs"], m
     return m
 
 
@@ -348,7 +360,7 @@ def oracle_half_adaln(aw, inp, ada, rows=None, temb6=None):
 def check_half(got, want, x, name):
     """The residual is fp32 (x + gate * block): compare the update
     gate * block, whose bf16 block carries the attention half's tolerance."""
-    check(got - x, want - x, name)
+    check(got - x, want - x, name, rounded=False)
 
 
 @pytest.mark.timeout(600)
