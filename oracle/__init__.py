@@ -282,6 +282,76 @@ def e4m3_values():
     return out
 
 
+def quantize_mx_rows(v):
+    """MX blocks of 32 along the last axis of fp64 values v [..., cols]:
+    (codes uint8 [..., cols], e8m0 bytes uint8 [..., cols // 32])."""
+    v = np.ascontiguousarray(v, np.float64)
+    rows, cols = int(np.prod(v.shape[:-1])), v.shape[-1]
+    assert cols % 32 == 0
+    q = np.empty(v.shape, np.uint8)
+    e8 = np.empty(v.shape[:-1] + (cols // 32,), np.uint8)
+    L = lib()
+    L.orc_quantize_mx_rows.argtypes = [ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 3
+    L.orc_quantize_mx_rows.restype = None
+    L.orc_quantize_mx_rows(rows, cols, _p(v), _p(q), _p(e8))
+    return q, e8
+
+
+def dequantize_mx_rows(q, e8):
+    """decode(q) * 2^(e8 - 127) per block of 32, fp64."""
+    q = np.ascontiguousarray(q, np.uint8)
+    e8 = np.ascontiguousarray(e8, np.uint8)
+    rows, cols = int(np.prod(q.shape[:-1])), q.shape[-1]
+    assert e8.shape == q.shape[:-1] + (cols // 32,)
+    v = np.empty(q.shape, np.float64)
+    L = lib()
+    L.orc_dequantize_mx_rows.argtypes = [ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 3
+    L.orc_dequantize_mx_rows.restype = None
+    L.orc_dequantize_mx_rows(rows, cols, _p(q), _p(e8), _p(v))
+    return v
+
+
+def act_to_mx(act):
+    """The fp8 activations of fp64 act values [..., I]: each value rounded to
+    bf16 (the act storage type of the block), then MX blocks of 32.  Returns
+    (codes, e8m0 bytes, dequantized values fp64)."""
+    q, e8 = quantize_mx_rows(bf16_round(act))
+    return q, e8, dequantize_mx_rows(q, e8)
+
+
+def w8a8_experts(wl, x, ids, w, w13, w2, shared_w13=None, shared_w2=None):
+    """Expert part of the block with fp8 weights and fp8 activations, for a
+    given routing (ids, w [n, K]; ids outside [0, E) are empty slots): the x
+    rows are quantized like weight rows (quantize_fp8_rows) and dequantized,
+    each slot's act (act_rows, fp64) goes through act_to_mx, then the down
+    projection and combine (down_combine).  w13, w2, shared_w13, shared_w2 are
+    the dequantized fp8 weights (dequantize_fp8_rows).  Returns out [n, H]
+    fp64."""
+    x = _f32(x)
+    ids = np.ascontiguousarray(ids, np.int32)
+    n, K, NS, E = x.shape[0], wl.top_k, wl.n_shared, wl.num_experts
+    KS = K + NS
+    xd = dequantize_fp8_rows(*quantize_fp8_rows(x))
+    slot_tok = np.repeat(np.arange(n, dtype=np.int32), KS).reshape(n, KS)
+    slot_seg = np.concatenate([ids, np.broadcast_to(E + np.arange(NS, dtype=np.int32), (n, NS))],
+                              axis=1)
+    valid = (slot_seg >= 0) & (slot_seg < E + NS)
+    act = act_rows(wl, xd, w13, shared_w13, slot_tok[valid], slot_seg[valid])
+    act_slots = np.zeros((n, KS, wl.intermediate), np.float32)
+    act_slots[valid] = act_to_mx(act)[2]
+    return down_combine(wl, act_slots, ids, w, w2, shared_w2)
+
+
+def moe_forward_w8a8(wl, x, router_w, e_bias, w13, w2, shared_w13=None, shared_w2=None,
+                     mask=None):
+    """Whole block with fp8 weights (given dequantized) and fp8 activations:
+    the router on x as in moe_forward, then w8a8_experts.  Returns dict(out
+    fp64, ids, w, m_grp, m_sel)."""
+    r = route(wl, x, router_w, e_bias, mask)
+    r["out"] = w8a8_experts(wl, x, r["ids"], r["w"], w13, w2, shared_w13, shared_w2)
+    return r
+
+
 def linear(x, w, b=None):
     """x [T, C] @ w[N, C]^T (+ b[N]) in fp64 (plain loops in C)."""
     x, w, b = _f32(x), _f32(w), _f32(b)

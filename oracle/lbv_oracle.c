@@ -575,6 +575,50 @@ void orc_e4m3_decode_all(double *out)
 }
 
 /* ---------------------------------------------------------------------------
+ * FP8 activations in MX blocks (OCP Microscaling, MXFP8 E4M3), for the
+ * expert path with fp8 weights and fp8 activations.  The pages name FP8
+ * expert backends but give no recipe (same source as above).  Reading: a row
+ * is cut into blocks of 32 consecutive values; a block has one scale 2^e kept
+ * as the e8m0 byte e + 127, e chosen by the rule of the weight rows above
+ * (smallest e with max|v| <= 448 * 2^e, e = 0 for an all-zero block) and held
+ * to [-127, 127], the byte's range; each value is the nearest e4m3fn code of
+ * v * 2^-e, ties to the even code.  (The MX specification takes
+ * e = floor(log2 max|v|) - 8 and saturates; the two agree unless
+ * 448 * 2^e < max|v| < 512 * 2^e, where this rule takes the next e and
+ * clips nothing.)
+ * ------------------------------------------------------------------------- */
+
+/* v [rows, cols] (cols a multiple of 32) -> codes q [rows, cols] and e8m0
+ * bytes e8 [rows, cols / 32]. */
+void orc_quantize_mx_rows(int64_t rows, int64_t cols, const double *v, uint8_t *q, uint8_t *e8)
+{
+    const int64_t nb = cols / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const double *vb = v + r * cols + b * 32;
+            double amax = 0.0;
+            for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs(vb[i]));
+            int e = fp8_row_exponent(amax);
+            if (e < -127) e = -127;
+            if (e > 127) e = 127;
+            e8[r * nb + b] = (uint8_t)(e + 127);
+            for (int i = 0; i < 32; ++i) q[r * cols + b * 32 + i] = e4m3_encode(ldexp(vb[i], -e));
+        }
+    }
+}
+
+/* v[r, c] = decode(q[r, c]) * 2^(e8[r, c / 32] - 127). */
+void orc_dequantize_mx_rows(int64_t rows, int64_t cols, const uint8_t *q, const uint8_t *e8,
+                            double *v)
+{
+    const int64_t nb = cols / 32;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c)
+            v[r * cols + c] = ldexp(e4m3_decode(q[r * cols + c]), (int)e8[r * nb + c / 32] - 127);
+}
+
+/* ---------------------------------------------------------------------------
  * The attention half of a LingBot-Video DiT layer (prhub summary of sglang PR
  * #32341, the LingBotVideoAttention excerpt under "关键源码片段" and "实现拆解"
  * step 2): q, k, v are linear projections of the layer input; q and k get an
