@@ -361,6 +361,36 @@ def main():
             "format": "e4m3fn codes, one power-of-two fp32 scale per weight row; bf16 "
                       "activations, fp32 accumulation",
         }
+
+        # fp8 weights and fp8 activations: both matmuls on the fp8 matrix cores
+        if H % 128 == 0 and I % 128 == 0 and I <= 1024:
+            def step_a8():
+                lbv.lbv_moe_forward_w8a8(cfg, x, mask, router_w, e_bias, wq, out, ids, wts, ws,
+                                         stream)
+
+            for _ in range(args.warmup):
+                step_a8()
+            torch.cuda.synchronize()
+            ea = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+            ea[0].record(stream)
+            for i in range(args.steps):
+                step_a8()
+                ea[i + 1].record(stream)
+            torch.cuda.synchronize()
+            msa = ea[0].elapsed_time(ea[-1]) / args.steps
+            pera = [ea[i].elapsed_time(ea[i + 1]) for i in range(args.steps)]
+            res["w8a8"] = {
+                "ms_per_step": msa,
+                "tokens_per_s": T / (msa * 1e-3),
+                "step_ms_median": pct(pera, 50),
+                "speedup_vs_bf16": ms_per_step / msa,
+                "speedup_vs_fp8_weights": ms8 / msa,
+                "matmul_flops": gemm_flops,
+                "format": "fp8 weights as above; x rows quantized like weight rows (one "
+                          "power-of-two scale per token); act rounded to bf16, then MX blocks "
+                          "of 32 (e4m3fn codes, e8m0 scale); scaled fp8 MFMA, fp32 "
+                          "accumulation",
+            }
         del wq
 
     # ---- the attention half of the layer on the same token layout -----------------

@@ -304,6 +304,27 @@ lbv_status lbv_moe_forward_fp8(const lbv_moe_config *cfg, int64_t T, const void 
                                float *topk_w_out, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * lbv_moe_forward with fp8 expert weights and fp8 activations, both matmuls
+ * on the fp8 matrix cores (same source and same silence about the recipe as
+ * above).  Reading taken: the router runs on x as before; each x row is
+ * quantized like a weight row (e4m3fn codes, one power-of-two scale per
+ * token); act = silu(gate) * up is rounded to bf16, its storage type in the
+ * block, then stored in MX blocks of 32 values along I (OCP Microscaling:
+ * e4m3fn codes and one e8m0 scale byte 2^(b - 127) per block, the block's
+ * exponent chosen like a weight row's, held to [-127, 127]); the down
+ * matmul reads those blocks; the expert outputs and the combine are as in
+ * lbv_moe_forward.  Products are exact, sums fp32.
+ * cfg->dtype must be LBV_BF16 (LBV_ERR_UNSUPPORTED otherwise); hidden and
+ * intermediate multiples of 128, intermediate at most 1024 (LBV_ERR_SHAPE
+ * otherwise); x, out bf16; wq as for lbv_moe_forward_fp8; ws:
+ * lbv_moe_workspace_size bytes (the quantized x and act live in it).
+ */
+lbv_status lbv_moe_forward_w8a8(const lbv_moe_config *cfg, int64_t T, const void *x,
+                                const uint8_t *mask, const float *router_w, const float *e_bias,
+                                const lbv_moe_fp8_weights *wq, void *out, int32_t *topk_ids_out,
+                                float *topk_w_out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * ---------------------------------------------------------------------------
  * The steps on either side of the block in a LingBot-Video DiT layer (prhub
  * summary of sglang PR #32341, "实现拆解" step 2: AdaLN through

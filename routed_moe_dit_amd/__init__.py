@@ -23,7 +23,8 @@ __all__ = [
     "lbv_moe_gemm_w13_silu",
     "lbv_moe_gemm_w2_combine", "lbv_moe_forward", "lbv_adaln_rmsnorm",
     "lbv_moe_ffn_adaln_workspace_size", "lbv_moe_ffn_adaln", "Fp8Weights",
-    "lbv_quantize_fp8_rows", "quantize_fp8_weights", "lbv_moe_forward_fp8", "AttnConfig",
+    "lbv_quantize_fp8_rows", "quantize_fp8_weights", "lbv_moe_forward_fp8",
+    "lbv_moe_forward_w8a8", "AttnConfig",
     "attn_config", "attn_sp", "lbv_attn_workspace_size", "lbv_linear_bf16", "lbv_attn_qk_prep",
     "lbv_attn_core", "lbv_attn_forward", "lbv_attn_half_adaln_workspace_size",
     "lbv_attn_half_adaln", "EXPORTS", "LIB_PATH",
@@ -44,7 +45,8 @@ EXPORTS = (
     "lbv_moe_w2_workspace_size", "lbv_moe_route", "lbv_moe_route_noalloc",
     "lbv_moe_permute", "lbv_moe_gemm_w13_silu", "lbv_moe_gemm_w2_combine", "lbv_moe_forward",
     "lbv_adaln_rmsnorm", "lbv_moe_ffn_adaln_workspace_size", "lbv_moe_ffn_adaln",
-    "lbv_quantize_fp8_rows", "lbv_moe_forward_fp8", "lbv_attn_workspace_size", "lbv_linear_bf16",
+    "lbv_quantize_fp8_rows", "lbv_moe_forward_fp8", "lbv_moe_forward_w8a8",
+    "lbv_attn_workspace_size", "lbv_linear_bf16",
     "lbv_attn_qk_prep", "lbv_attn_core", "lbv_attn_forward", "lbv_attn_half_adaln_workspace_size",
     "lbv_attn_half_adaln",
 )
@@ -160,9 +162,9 @@ def load():
     L.lbv_moe_ffn_adaln.restype = st
     L.lbv_quantize_fp8_rows.argtypes = [P, ctypes.c_int32, I64, I64, P, P, P]
     L.lbv_quantize_fp8_rows.restype = st
-    L.lbv_moe_forward_fp8.argtypes = [C, I64, P, P, P, P, ctypes.POINTER(_Fp8WeightsC), P, P, P,
-                                      P, SZ, P]
-    L.lbv_moe_forward_fp8.restype = st
+    for n in ("lbv_moe_forward_fp8", "lbv_moe_forward_w8a8"):
+        getattr(L, n).argtypes = [C, I64, P, P, P, P, ctypes.POINTER(_Fp8WeightsC), P, P, P, P, SZ, P]
+        getattr(L, n).restype = st
     A = ctypes.POINTER(AttnConfig)
     L.lbv_attn_workspace_size.argtypes = [A, I64, I64, ctypes.POINTER(SZ)]
     L.lbv_attn_workspace_size.restype = st
@@ -542,6 +544,20 @@ def quantize_fp8_weights(w13, w2, shared_w13=None, shared_w2=None, stream=None) 
 
 def lbv_moe_forward_fp8(cfg, x, mask, router_w, e_bias, wq: Fp8Weights, out, topk_ids_out,
                         topk_w_out, ws, stream=None):
+    """lbv_moe_forward with fp8 expert weights (bf16 activations)."""
+    _forward_fp8_weights("lbv_moe_forward_fp8", cfg, x, mask, router_w, e_bias, wq, out,
+                         topk_ids_out, topk_w_out, ws, stream)
+
+
+def lbv_moe_forward_w8a8(cfg, x, mask, router_w, e_bias, wq: Fp8Weights, out, topk_ids_out,
+                         topk_w_out, ws, stream=None):
+    """lbv_moe_forward with fp8 expert weights and fp8 activations."""
+    _forward_fp8_weights("lbv_moe_forward_w8a8", cfg, x, mask, router_w, e_bias, wq, out,
+                         topk_ids_out, topk_w_out, ws, stream)
+
+
+def _forward_fp8_weights(fn, cfg, x, mask, router_w, e_bias, wq, out, topk_ids_out, topk_w_out,
+                         ws, stream):
     H, E, K, I, ns, KS, S = _dims(cfg)
     _shape(x, "x", None, H)
     T = x.shape[0]
@@ -570,12 +586,12 @@ def lbv_moe_forward_fp8(cfg, x, mask, router_w, e_bias, wq: Fp8Weights, out, top
             for t, n in zip(wq.tensors(), names)]
     cw = _Fp8WeightsC(*ptrs)
     dt = cfg.torch_dtype
-    _check(load().lbv_moe_forward_fp8(
+    _check(getattr(load(), fn)(
         ctypes.byref(cfg), T, _ptr(x, "x", dt), _ptr(mask, "mask", torch.uint8),
         _ptr(router_w, "router_w", torch.float32), _ptr(e_bias, "e_bias", torch.float32),
         ctypes.byref(cw), _ptr(out, "out", dt), _ptr(topk_ids_out, "topk_ids_out", torch.int32),
         _ptr(topk_w_out, "topk_w_out", torch.float32), _ptr(ws, "ws"),
-        ws.numel() * ws.element_size(), _stream(stream)), "lbv_moe_forward_fp8")
+        ws.numel() * ws.element_size(), _stream(stream)), fn)
 
 
 def lbv_attn_workspace_size(cfg: AttnConfig, B: int, S: int) -> int:

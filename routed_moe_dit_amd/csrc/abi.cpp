@@ -13,7 +13,7 @@ using lbv::Dims;
 
 namespace {
 
-constexpr int32_t kAbiVersion = 5;
+constexpr int32_t kAbiVersion = 6;
 constexpr size_t kAlign = 256;
 
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -453,6 +453,70 @@ lbv_status lbv_moe_forward_fp8(const lbv_moe_config* cfg, int64_t T, const void*
     if (e == hipSuccess)
         e = lbv::launch_gemm_w2(d, act, wq->w2, wq->shared_w2, offsets, sorted, y, ctr2, stream,
                                 wq->w2_scale, wq->shared_w2_scale, false);
+    if (e == hipSuccess) e = lbv::launch_combine(d, y, inv, w, out, stream);
+    return hip_status(e);
+}
+
+lbv_status lbv_moe_forward_w8a8(const lbv_moe_config* cfg, int64_t T, const void* x,
+                                const uint8_t* mask, const float* router_w, const float* e_bias,
+                                const lbv_moe_fp8_weights* wq, void* out, int32_t* topk_ids_out,
+                                float* topk_w_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    Dims d;
+    lbv_status st = make_dims(cfg, T, &d);
+    if (st != LBV_OK) return st;
+    if (!d.bf16) return LBV_ERR_UNSUPPORTED;
+    // k-tiles of 128 values; act's block scales take kA8ScalePitch bytes per row
+    if (d.H % 128 != 0 || d.I % 128 != 0 || d.I > 32 * lbv::kA8ScalePitch) return LBV_ERR_SHAPE;
+    if (T == 0) return LBV_OK;
+    if (!wq) return LBV_ERR_NULL;
+    if (!x || !router_w || !e_bias || !wq->w13 || !wq->w13_scale || !wq->w2 || !wq->w2_scale ||
+        !out || !ws)
+        return LBV_ERR_NULL;
+    if (d.NS > 0 && (!wq->shared_w13 || !wq->shared_w13_scale || !wq->shared_w2 ||
+                     !wq->shared_w2_scale))
+        return LBV_ERR_NULL;
+    if (!aligned16(x) || !aligned16(router_w) || !aligned4(e_bias) || !aligned16(wq->w13) ||
+        !aligned16(wq->w2) || !aligned16(wq->shared_w13) || !aligned16(wq->shared_w2) ||
+        !aligned4(wq->w13_scale) || !aligned4(wq->w2_scale) || !aligned4(wq->shared_w13_scale) ||
+        !aligned4(wq->shared_w2_scale) || !aligned16(out) || !aligned16(ws) ||
+        !aligned4(topk_ids_out) || !aligned4(topk_w_out))
+        return LBV_ERR_ALIGN;
+    const size_t xbytes = static_cast<size_t>(T) * d.H * 2;
+    if (overlaps(x, xbytes, out, xbytes)) return LBV_ERR_ALIAS;
+    const FwdLayout L = fwd_layout(d);
+    if (ws_bytes < L.total) return LBV_ERR_WORKSPACE;
+
+    char* base = static_cast<char*>(ws);
+    int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(base + L.ids);
+    float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(base + L.w);
+    int32_t* offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+    int32_t* sorted = reinterpret_cast<int32_t*>(base + L.sorted);
+    int32_t* inv = reinterpret_cast<int32_t*>(base + L.inv);
+    int* ctr1 = reinterpret_cast<int*>(base + L.ctr1);
+    int* ctr2 = reinterpret_cast<int*>(base + L.ctr2);
+    // fp8 act [R, I] and its block scales [R, kA8ScalePitch] in the bf16 act
+    // region (R I + 32 R <= 2 R I bytes as I >= 128); fp8 x [T, H] and its
+    // scales [T] in the y region, which the down matmul fills only after the
+    // gate/up matmul has read them (R (K + ns) H 2 >= T H + 4 T bytes)
+    const size_t R = static_cast<size_t>(T) * d.KS;
+    uint8_t* actq = reinterpret_cast<uint8_t*>(base + L.act);
+    uint8_t* act_scales = actq + R * d.I;
+    uint8_t* xq = reinterpret_cast<uint8_t*>(base + L.y);
+    float* xs = reinterpret_cast<float*>(xq + static_cast<size_t>(T) * d.H);
+    void* y = base + L.y;
+
+    hipError_t e = lbv::launch_route(d, x, router_w, e_bias, mask, ids, w, base + L.route, stream);
+    // the permutation's scan zeroes both matmuls' tile queue counters
+    if (e == hipSuccess)
+        e = lbv::launch_permute(d, ids, offsets, sorted, inv, base + L.perm, stream, ctr1, ctr2);
+    if (e == hipSuccess) e = lbv::launch_quantize_fp8(x, 1, T, d.H, xq, xs, stream);
+    if (e == hipSuccess)
+        e = lbv::launch_gemm_w13_a8(d, xq, xs, wq->w13, wq->w13_scale, wq->shared_w13,
+                                    wq->shared_w13_scale, offsets, sorted, actq, act_scales, ctr1,
+                                    stream);
+    if (e == hipSuccess)
+        e = lbv::launch_gemm_w2_a8(d, actq, act_scales, wq->w2, wq->w2_scale, wq->shared_w2,
+                                   wq->shared_w2_scale, offsets, sorted, y, ctr2, stream);
     if (e == hipSuccess) e = lbv::launch_combine(d, y, inv, w, out, stream);
     return hip_status(e);
 }

@@ -111,6 +111,14 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// The 32-byte fp8 MFMA operand made of two 16-byte fragments (low, high).
+__device__ __forceinline__ i32x8 op8(const bf16x8& lo8, const bf16x8& hi8) {
+    const i32x4 l4 = __builtin_bit_cast(i32x4, lo8), h4 = __builtin_bit_cast(i32x4, hi8);
+    return __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
 struct GemmArgs {
     const void* A;          // gate/up: x [T, H];  down: act [rows, I]
@@ -119,6 +127,9 @@ struct GemmArgs {
     const float* Bs;        // fp8 weights: row scales of B ([E, 2I] / [E, H])
     const float* Bshs;      // fp8 weights: row scales of Bsh ([2 Is] / [H])
     const float* bias;      // dense down-style matmul: [ncols] fp32 added before rounding, or null
+    const float* xs;        // fp8 tokens, gate/up: x's power-of-two scale per token [T]
+    uint8_t* asc;           // fp8 tokens: act's MX block scales [rows, kA8ScalePitch]
+                            // (written by gate/up, read by down)
     const int32_t* offsets; // [S + 1]
     const int32_t* rows;    // sorted_rows: slot id of each sorted row
     void* C;                // gate/up: act [rows, I];  down: y [rows, H]
@@ -201,9 +212,19 @@ constexpr int kMaxSeg = 512;
 // DENSE (down-style only): one segment whose rows are stored in order (no
 // slot ids) and an optional fp32 bias per output column: a plain linear layer
 // y = x W^T + b.
-template <int BM, int BN, int MODE, int NW, int CWV, int ORDER, int STG, bool W8, bool DENSE>
+template <int BM, int BN, int MODE, int NW, int CWV, int ORDER, int STG, bool W8, bool DENSE,
+          bool A8 = false>
 __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     static_assert(!DENSE || MODE == 1, "dense rows: down-style only");
+    // A8: fp8 tokens and fp8 weights on the scaled fp8 MFMA.  Weights: e4m3fn
+    // codes with a power-of-two scale per row; gate/up tokens: x's codes with
+    // a power-of-two scale per token; down tokens: act in MX blocks of 32
+    // (e4m3fn codes, an e8m0 scale per block), which the gate/up epilogue
+    // writes.  The row scales are applied in the epilogues, the act block
+    // scales by the MFMA.  A k-tile holds 128 values per row, so its rows are
+    // 128 bytes, as a bf16 k-tile of 64: the same stages and copies.
+    static_assert(!A8 || (!W8 && !DENSE && (BM == 128 || BM == 192 || BM == 256) && NW == 8 && CWV == 4 && STG == 2),
+                  "fp8 tokens: 128-, 192- or 256-row tiles, 8 waves, 2 stages");
     // NW waves: 2 along the tokens x NW/2 along the weight rows (NW = 4: one
     // wave per SIMD with 128 x 128 accumulators; NW = 8: two per SIMD with
     // 128 x 64, so that one wave's MFMAs can cover the other's waits).
@@ -221,7 +242,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     constexpr int RPI = 64 / CPR;                // A rows per 1 KB copy instruction
     constexpr int CPRB = BKB / 8;                // ... per B row
     constexpr int RPIB = 64 / CPRB;              // B rows per 1 KB copy instruction
-    constexpr int EB = W8 ? 1 : 2;               // bytes per weight element in HBM
+    constexpr int EB = W8 || A8 ? 1 : 2;         // bytes per weight element in HBM
     // Waves 0 .. CW-1 issue the stage copies (with NW = 8 and CW = 4 one wave
     // per SIMD copies while the other only multiplies).
     constexpr int CW = CWV < NW ? CWV : NW;
@@ -244,6 +265,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     __shared__ int s_rid[BM];                    // slot ids of a tile's rows: gate/up: the next tile's; down: this tile's
     __shared__ int s_tmp[8];
     __shared__ int s_claim[2];
+    // A8: the scales of a tile, two buffers (tile parity): its weight rows,
+    // its token rows (gate/up: x's scale per token) and its act rows' block
+    // scales (down: kA8ScalePitch bytes per row)
+    __shared__ float s_sw[A8 ? 2 * BN : 1];
+    __shared__ float s_sx[A8 && MODE == 0 ? 2 * BM : 1];
+    __shared__ __attribute__((aligned(16))) uint8_t s_as[A8 && MODE == 1 ? 2 * BM * kA8ScalePitch : 16];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -396,7 +423,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
             abase = static_cast<const uint16_t*>(a.A);
             bbase = shared_seg ? Bsh : B + static_cast<int64_t>(seg_) * 2 * a.I * a.H * EB;
         } else {
-            abase = static_cast<const uint16_t*>(a.A) + static_cast<int64_t>(seg_r0_) * a.I;
+            abase = static_cast<const uint16_t*>(a.A) + static_cast<int64_t>(seg_r0_) * (A8 ? a.I / 2 : a.I);
             bbase = shared_seg ? Bsh + jsh * a.I * EB : B + static_cast<int64_t>(seg_) * a.H * a.I * EB;
         }
 #pragma unroll
@@ -406,11 +433,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
             if (MODE == 0) {
                 int tok = s_rid[r] / a.KS;
                 tok = tok < 0 ? 0 : (tok >= a.T ? static_cast<int>(a.T) - 1 : tok);
-                aoff[i] = (__umul24(tok, a.H) + c * 8) * 2;
+                aoff[i] = A8 ? __umul24(tok, a.H) + c * 16 : (__umul24(tok, a.H) + c * 8) * 2;
             } else {
                 int m = m0_ + r;
                 if (m >= seg_n_) m = seg_n_ - 1;
-                aoff[i] = (__umul24(m, a.I) + c * 8) * 2;
+                aoff[i] = A8 ? __umul24(m, a.I) + c * 16 : (__umul24(m, a.I) + c * 8) * 2;
             }
         }
 #pragma unroll
@@ -472,9 +499,59 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         }
     };
 
+    // A8: the scales tile (seg_, m0_, nt_) needs, copied into buffer buf by
+    // the copying waves and counted by the same waits as the stage copies:
+    // one 4-byte copy per weight row and per token row (gate/up: the token
+    // ids come from s_rid, which must have landed), the act rows' block
+    // scales (down) as 1 KB pieces of one contiguous run.  Rows past the
+    // tile's segment take clamped rows (their outputs are not stored).
+    auto scale_copy = [&](int buf, int seg_, int seg_r0_, int m0_, int nt_, int lo_, int hi_) {
+        if constexpr (A8) {
+            if (wave >= CW) return;
+            const int ln = (threadIdx.x & 63) + opaque_zero();
+            const bool shared_seg = seg_ >= a.E;
+            const int jsh = seg_ - a.E;
+            const int r = wave * 64 + ln;                     // row r of the tile's B (and A) rows
+            int idx;
+            if (MODE == 0) {
+                const int half = r / (BN / 2);
+                int n = nt_ * (BN / 2) + (r % (BN / 2));
+                n = n < lo_ ? lo_ : (n > hi_ ? hi_ : n);
+                if (n >= a.I) n = a.I - 1;
+                idx = shared_seg ? (half ? Is + jsh * a.I + n : jsh * a.I + n)
+                                 : seg_ * 2 * a.I + (half ? a.I + n : n);
+            } else {
+                int n = nt_ * BN + r;
+                n = n < lo_ ? lo_ : (n > hi_ ? hi_ : n);
+                if (n >= a.H) n = a.H - 1;
+                idx = shared_seg ? n : seg_ * a.H + n;
+            }
+            lds_dma4_sb(shared_seg ? a.Bshs : a.Bs, static_cast<uint32_t>(idx) * 4,
+                        lds_addr(&s_sw[buf * BN + wave * 64]));
+            if constexpr (MODE == 0) {
+                if (wave < BM / 64) {
+                    int tok = s_rid[r] / a.KS;
+                    tok = tok < 0 ? 0 : (tok >= a.T ? static_cast<int>(a.T) - 1 : tok);
+                    lds_dma4_sb(a.xs, static_cast<uint32_t>(tok) * 4, lds_addr(&s_sx[buf * BM + wave * 64]));
+                }
+            } else {
+                constexpr int NP = BM * kA8ScalePitch / 1024;   // 1 KB pieces
+                const int64_t last = a.T * a.KS * kA8ScalePitch - 16;
+#pragma unroll
+                for (int d = 0; d < NP; ++d) {
+                    if (d % CW != wave) continue;
+                    int64_t off = (static_cast<int64_t>(seg_r0_) + m0_) * kA8ScalePitch + d * 1024 + ln * 16;
+                    off = off < last ? off : last;
+                    lds_dma16_sb<0>(a.asc, static_cast<uint32_t>(off),
+                                    lds_addr(s_as + buf * BM * kA8ScalePitch + d * 1024));
+                }
+            }
+        }
+    };
+
     const int a_lds = wave * (BM / CW) * BK;     // this wave's rows inside an A / B part
     const int b_lds = wave * (BN / CW) * BKB;
-    const int nk = a.kdim / BK;
+    const int nk = a.kdim / (A8 ? 2 * BK : BK);  // k-tiles (A8: 128 one-byte values per row)
     // the k-loop of a tile runs over nkp = nk rounded up to a multiple of STG,
     // so that every step of an iteration is unconditional (no MFMA under a
     // branch); the k-tiles past nk are zero-filled stages, whose products add
@@ -595,6 +672,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     }
     set_sources(seg, seg_r0, seg_n, m0, nt, lo, hi);
     load_scales(seg, nt, lo, hi, sc);
+    scale_copy(0, seg, seg_r0, m0, nt, lo, hi);
     // k-tiles 0 .. STG-2 into stages 0 .. STG-2 (zero-filled past nk)
     auto pro_fill = [&](auto S, int kt) {
         if (kt < nk) {
@@ -613,6 +691,45 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     for (int i = 0; i < TM; ++i) tf0[i] = *reinterpret_cast<const bf16x8*>(fa[0] + i * 32 * BK);
 #pragma unroll
     for (int j = 0; j < TN; ++j) read_b(wf0, j, 0, 0);
+    // A8: slice 1 as well (a step multiplies two slices), and the act block
+    // scales of k-tile 0
+    uint32_t asc[TM], asn[TM];
+    // The act row's block scales of k-tile kt, for step 0 (low byte) and
+    // step 1 (next byte): blocks 4kt + khalf and 4kt + 2 + khalf, stored at
+    // bytes 4kt + 2 khalf and 4kt + 2 khalf + 1 (the gate/up epilogue writes
+    // each k-tile's four blocks in the order 0, 2, 1, 3).
+    const uint8_t* const as_lane = s_as + (wm * (BM / 2) + (lane & 31)) * kA8ScalePitch + 2 * khalf;
+    auto read_asc = [&](uint32_t* dst, int buf, int kt) {
+        if constexpr (A8 && MODE == 1) {
+            kt = kt < nk ? kt : nk - 1;
+            const uint8_t* p = as_lane + buf * BM * kA8ScalePitch + 4 * kt;
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                dst[i] = *reinterpret_cast<const uint16_t*>(p + i * 32 * kA8ScalePitch);
+        }
+    };
+    // A8 fragments: 32-byte operands (slices 2s and 2s + 1 of a k-tile), two
+    // sets: step 0 of a k-tile multiplies set P while set Q is read, step 1
+    // multiplies Q while P is read (as the bf16 slices alternate), so the same
+    // registers hold the same set at every step and across the loop.
+    i32x8 tqP[TM], wqP[TN], tqQ[TM], wqQ[TN];
+    auto rd8 = [](const uint16_t* p0, const uint16_t* p1) -> i32x8 {
+        return op8(*reinterpret_cast<const bf16x8*>(p0), *reinterpret_cast<const bf16x8*>(p1));
+    };
+    // fragment read r (token fragments first) of step s2 / 2 of the k-tile
+    // in `stage` into the set (T8, W8_)
+    auto rd_frag = [&](i32x8* T8, i32x8* W8_, int r, int stage, int s2) {
+        if (r < TM)
+            T8[r] = rd8(fa[s2] + stage * ASZ + r * 32 * BK, fa[s2 + 1] + stage * ASZ + r * 32 * BK);
+        else
+            W8_[r - TM] = rd8(fb[s2] + stage * BSZ + brow(r - TM) * BKB,
+                              fb[s2 + 1] + stage * BSZ + brow(r - TM) * BKB);
+    };
+    if constexpr (A8) {
+#pragma unroll
+        for (int r = 0; r < TM + TN; ++r) rd_frag(tqP, wqP, r, 0, 0);
+        read_asc(asc, 0, 0);
+    }
 
     constexpr int NQ = TM * TN;                  // MFMAs per slice
     constexpr int NR = TM + TN;                  // fragment reads per slice
@@ -719,6 +836,96 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     };
 #undef LBV_SLICE
 
+    // A8: one k-tile (128 values per row) in stage S = kt % 2, two MFMA steps.
+    // Step s multiplies 32-byte fragments made of slices 2s and 2s + 1: a
+    // lane's chunks 4s + khalf and 4s + 2 + khalf, i.e. values k = 64s + 16
+    // khalf + [0, 16) and 64s + 32 + 16 khalf + [0, 16), the instruction's own
+    // order.  After MFMA r of a step comes fragment read r of the other set
+    // (reads left over after the last MFMA).  Step 0 (set P) reads set Q from
+    // slices 2, 3 and carries the copies of k-tile kt + 1; step 1 (set Q)
+    // issues NPRE8 MFMAs, waits for k-tile kt + 1 and passes the barrier, then
+    // issues the rest with the reads of k-tile kt + 1's slices 0, 1 into P.
+    // The down matmul's act block scales: in step s, lane l provides the
+    // scale of block 4kt + 2s + khalf of token row l % 32 in byte 0 of its
+    // scale operand; read_asc brings both steps' bytes in one 16-bit word.
+    constexpr int NR8 = TM + TN;                 // tuple reads per step
+    constexpr int NPRE8 = NQ > NR8 ? NQ - NR8 : 0;
+#define LBV_MFMA8(Q, SIDX, TS8, WS8)                                                          \
+    {                                                                                          \
+        const int sbv_ = MODE == 1 ? static_cast<int>(asc[(Q) % TM] >> (8 * (SIDX))) : 127;  \
+        acc[(Q) / TM][(Q) % TM] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(              \
+            WS8[(Q) / TM], TS8[(Q) % TM], acc[(Q) / TM][(Q) % TM], 0, 0, 0, 127, 0, sbv_);     \
+    }
+    // stage given at run time (one k-tile per loop iteration): its parts and
+    // the copies and zero fill of stage s_
+    auto copy8 = [&](int s_, int kt_, auto D) {
+        constexpr int d = decltype(D)::value;
+        if (wave >= CW) return;
+        if constexpr (d < AI)
+            lds_dma16_sb<d * RPI * BK * 2>(abase + kt_ * BK, aoff[d], lds_addr(lds + s_ * ASZ + a_lds));
+        else
+            lds_dma16_sb<(d - AI) * RPIB * BKB * 2>(bbase + kt_ * BKB * 2, boff[d - AI],
+                                                    lds_addr(lds + STG * ASZ + s_ * BSZ + b_lds));
+    };
+    auto zero_fill8 = [&](int s_) {
+        u32x4* pa = reinterpret_cast<u32x4*>(lds + s_ * ASZ);
+        u32x4* pb = reinterpret_cast<u32x4*>(lds + STG * ASZ + s_ * BSZ);
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int q = 0; q < ASZ / 8 / NTH; ++q) pa[tid + NTH * q] = z;
+#pragma unroll
+        for (int q = 0; q < BSZ / 8 / NTH; ++q) pb[tid + NTH * q] = z;
+    };
+    auto step8 = [&](int kt) {
+        const int cur = kt & 1, nxt = cur ^ 1;   // STG == 2
+        const int kf = kt + 1;                   // k-tile copied during this k-tile
+        const bool nextc = kf >= nkp;            // ... a k-tile of the next tile
+        const int kc = nextc ? kf - nkp : kf;
+        const bool want = !nextc || has_next;
+        const bool do_copy = want && kc < nk;
+        if (want && kc >= nk) zero_fill8(nxt);
+        if (MODE == 0 && kt == 0 && has_next) rid_copy(nseg_r0, nseg_n, nm0);
+        if (MODE == 1 && kt == 0) rid_copy(seg_r0, seg_n, m0);
+        // step 0: set P, reads of slices 2, 3 into Q, the copies
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            LBV_MFMA8(q, 0, tqP, wqP)
+#pragma unroll
+            for (int r = 0; r < NR8; ++r)
+                if ((r < NQ ? r : NQ - 1) == q) rd_frag(tqQ, wqQ, r, cur, 2);
+            static_for<NI>([&](auto D) {
+                if (decltype(D)::value * NQ / NI == q && do_copy) copy8(nxt, kc, D);
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // step 1: set Q; the hand-over after NPRE8 MFMAs
+#pragma unroll
+        for (int q = 0; q < NPRE8; ++q) {
+            LBV_MFMA8(q, 1, tqQ, wqQ)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (kt + 1 < nkp) wait_vmcnt<0>();       // k-tile kt + 1 (and any slot-id copy) landed
+        wait_lgkmcnt0();
+        block_barrier();
+        if (kt == nkp - STG && has_next) {
+            set_sources(nseg, nseg_r0, nseg_n, nm0, nnt, nlo, nhi);
+            scale_copy((it + 1) & 1, nseg, nseg_r0, nm0, nnt, nlo, nhi);
+        }
+        read_asc(asn, it & 1, kt + 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = NPRE8; q < NQ; ++q) {
+            LBV_MFMA8(q, 1, tqQ, wqQ)
+#pragma unroll
+            for (int r = 0; r < NR8; ++r)
+                if ((r < NQ - NPRE8 ? r : NQ - NPRE8 - 1) == q - NPRE8) rd_frag(tqP, wqP, r, nxt, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i) asc[i] = asn[i];
+    };
+#undef LBV_MFMA8
+
     constexpr int WCOLS = MODE == 0 ? BN / 2 / WN : BN / WN;   // output columns per wave
     constexpr int CHUNKS = WCOLS / 8;                    // 16-byte chunks per row
     // staging regions in stage STG-1 (the last one a tile reads): its A and B
@@ -727,7 +934,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     constexpr bool SPLIT = !W8 && ASZ == BSZ;
     constexpr int RSZ = W8 ? EPW : SPLIT ? 2 * ASZ / NW : BSZ / NW;   // staging elements per wave
     constexpr int PT0 = RSZ / WCOLS / 32;
-    constexpr int PT = PT0 < TM ? PT0 : TM;              // token tiles per staging pass
+    // token tiles per staging pass: the largest divisor of TM that fits
+    constexpr int PT = (PT0 >= TM) ? TM : (TM % PT0 == 0 ? PT0 : (PT0 >= 2 && TM % 2 == 0 ? 2 : 1));
     constexpr int PROWS = PT * 32;                       // rows per staging pass
     static_assert(PT >= 1 && TM % PT == 0, "whole token tiles per pass");
     constexpr int SL = STG - 1;
@@ -753,10 +961,15 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int i = 0; i < TM; ++i) acc[j][i] = f32x16{};
-        for (int kt = 0; kt < nkp; kt += STG) {
-            step(S0{}, kt, std::false_type{});
-            step(S1{}, kt + 1, std::false_type{});
-            if constexpr (STG == 3) step(S2{}, kt + 2, std::false_type{});
+        if constexpr (A8) {
+#pragma nounroll
+            for (int kt = 0; kt < nkp; ++kt) step8(kt);
+        } else {
+            for (int kt = 0; kt < nkp; kt += STG) {
+                step(S0{}, kt, std::false_type{});
+                step(S1{}, kt + 1, std::false_type{});
+                if constexpr (STG == 3) step(S2{}, kt + 2, std::false_type{});
+            }
         }
 
         // the claim issued at this tile's start (read at the start of the next
@@ -790,11 +1003,19 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             if (MODE == 0) {
-                                const float g = acc[j][i][4 * q + e];
-                                const float u = acc[j + TN / 2][i][4 * q + e];
+                                float g = acc[j][i][4 * q + e];
+                                float u = acc[j + TN / 2][i][4 * q + e];
+                                if constexpr (A8) {
+                                    // weight row scales (gate row, up row) and the token's scale
+                                    const int wr = (it & 1) * BN + wn * (BN / 2 / WN) + col + e;
+                                    const float sx = s_sx[(it & 1) * BM + wm * (BM / 2) + i * 32 + (elane & 31)];
+                                    g *= s_sw[wr] * sx;
+                                    u *= s_sw[wr + BN / 2] * sx;
+                                }
                                 v[e] = g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
                             } else {
                                 v[e] = acc[j][i][4 * q + e];
+                                if constexpr (A8) v[e] *= s_sw[(it & 1) * BN + wn * (BN / WN) + col + e];
                                 if (DENSE && a.bias) {
                                     const int bc = col0 + col + e;
                                     v[e] += a.bias[bc < ncols_all ? bc : ncols_all - 1];
@@ -821,7 +1042,50 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
                 const u32x4 v = *reinterpret_cast<const u32x4*>(ep + ep_off(row, ch * 8));
                 // gate/up: act rows in segment order; down: y rows in slot order
                 const int64_t orow = MODE == 0 || DENSE ? seg_r0 + m : s_rid[wm * (BM / 2) + p * PROWS + row];
-                if (m < seg_n && col >= lo && col <= hi) {
+                if constexpr (A8 && MODE == 0) {
+                    // act in MX blocks: 4 consecutive lanes hold 32 columns of
+                    // a row (4 chunks of 8), one block; its scale 2^e, e the
+                    // smallest integer with max|act| <= 448 2^e (0 for an
+                    // all-zero block, held to [-127, 127]); codes are the
+                    // nearest e4m3fn values of act 2^-e (ties to even)
+                    static_assert(CHUNKS % 4 == 0, "whole MX blocks per row and wave");
+                    float f[8];
+#pragma unroll
+                    for (int wi = 0; wi < 4; ++wi) {
+                        f[2 * wi] = __uint_as_float(v[wi] << 16);
+                        f[2 * wi + 1] = __uint_as_float(v[wi] & 0xffff0000u);
+                    }
+                    float amax = 0.0f;
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(f[k]));
+                    amax = fmaxf(amax, __shfl_xor(amax, 1));
+                    amax = fmaxf(amax, __shfl_xor(amax, 2));
+                    int ex = 0;
+                    if (amax > 0.0f) {
+                        int x;
+                        const float fr = frexpf(amax, &x);       // amax = fr 2^x, 448 = 0.875 2^9
+                        ex = fr <= 0.875f ? x - 9 : x - 8;
+                        ex = ex < -127 ? -127 : (ex > 127 ? 127 : ex);
+                    }
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) f[k] = fminf(fmaxf(ldexpf(f[k], -ex), -448.0f), 448.0f);
+                    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+                    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], w0, true);
+                    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+                    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], w1, true);
+                    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+                    const u32x2 o8 = {static_cast<unsigned>(w0), static_cast<unsigned>(w1)};
+                    if (m < seg_n && col >= lo && col <= hi) {
+                        uint8_t* C8 = static_cast<uint8_t*>(a.C);
+                        u32x2* dst = reinterpret_cast<u32x2*>(C8 + orow * ncols + col);
+                        if (LBV_G1_EPI_NT) __builtin_nontemporal_store(o8, dst);
+                        else *dst = o8;
+                        // blocks 4g + (0, 1, 2, 3) of a row at bytes 4g + (0, 2, 1, 3)
+                        const int kb = col / 32;
+                        const int pos = (kb & ~3) | ((kb & 1) << 1) | ((kb >> 1) & 1);
+                        if ((ch & 3) == 0) a.asc[orow * kA8ScalePitch + pos] = static_cast<uint8_t>(ex + 127);
+                    }
+                } else if (m < seg_n && col >= lo && col <= hi) {
                     u32x4* dst = reinterpret_cast<u32x4*>(C + orow * ncols + col);
                     if (MODE == 0 ? LBV_G1_EPI_NT : LBV_G2_EPI_NT) __builtin_nontemporal_store(v, dst);
                     else *dst = v;
@@ -844,6 +1108,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
         for (int i = 0; i < TM; ++i) tf0[i] = *reinterpret_cast<const bf16x8*>(fa[0] + i * 32 * BK);
 #pragma unroll
         for (int j = 0; j < TN; ++j) read_b(wf0, j, 0, 0);
+        if constexpr (A8) {
+#pragma unroll
+            for (int r = 0; r < TM + TN; ++r) rd_frag(tqP, wqP, r, 0, 0);
+            read_asc(asc, (it + 1) & 1, 0);
+        }
         t = tn;
         ++it;
         seg = nseg;
@@ -1180,6 +1449,58 @@ hipError_t launch_gemm_w2(const Dims& d, const void* act, const void* w2, const 
         hipLaunchKernelGGL(gemm_f32_kernel<1>, dim3(static_cast<unsigned>(grid)), dim3(256), 0,
                            stream, a);
     }
+    return hipGetLastError();
+}
+
+#ifndef LBV_A8_BM
+#define LBV_A8_BM 192
+#endif
+
+hipError_t launch_gemm_w13_a8(const Dims& d, const uint8_t* xq, const float* xs,
+                              const void* w13, const float* w13_scale, const void* shared_w13,
+                              const float* shared_w13_scale, const int32_t* offsets,
+                              const int32_t* sorted_rows, uint8_t* actq, uint8_t* act_scales,
+                              int* ctr, hipStream_t stream) {
+    GemmArgs a = make_args(d);
+    a.ctr = ctr;
+    a.A = xq;
+    a.xs = xs;
+    a.B = w13;
+    a.Bsh = shared_w13;
+    a.Bs = w13_scale;
+    a.Bshs = shared_w13_scale;
+    a.offsets = offsets;
+    a.rows = sorted_rows;
+    a.C = actq;
+    a.asc = act_scales;
+    a.kdim = d.H;
+    a.ncols = d.I;
+    a.ntn = (d.I + G1_BN / 2 - 1) / (G1_BN / 2);
+    hipLaunchKernelGGL((gemm_bf16_kernel<LBV_A8_BM, G1_BN, 0, 8, 4, LBV_G1_ORDER, 2, false, false, true>),
+                       dim3(cu_count() / 8 * 8), dim3(512), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_w2_a8(const Dims& d, const uint8_t* actq, uint8_t* act_scales,
+                             const void* w2, const float* w2_scale, const void* shared_w2,
+                             const float* shared_w2_scale, const int32_t* offsets,
+                             const int32_t* sorted_rows, void* y, int* ctr, hipStream_t stream) {
+    GemmArgs a = make_args(d);
+    a.ctr = ctr;
+    a.A = actq;
+    a.asc = act_scales;
+    a.B = w2;
+    a.Bsh = shared_w2;
+    a.Bs = w2_scale;
+    a.Bshs = shared_w2_scale;
+    a.offsets = offsets;
+    a.rows = sorted_rows;                        // y is stored in slot order
+    a.C = y;
+    a.kdim = d.I;
+    a.ncols = d.H;
+    a.ntn = (d.H + G2_BN - 1) / G2_BN;         // a partial last n-tile (H = 128 mod 256) is clamped
+    hipLaunchKernelGGL((gemm_bf16_kernel<LBV_A8_BM, G2_BN, 1, 8, 4, LBV_G2_ORDER, 2, false, false, true>),
+                       dim3(cu_count() / 8 * 8), dim3(512), 0, stream, a);
     return hipGetLastError();
 }
 

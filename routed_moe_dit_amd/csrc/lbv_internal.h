@@ -90,6 +90,27 @@ hipError_t launch_gemm_w2(const Dims& d, const void* act, const void* w2, const 
 hipError_t launch_quantize_fp8(const void* w, int src_bf16, int64_t rows, int cols, uint8_t* q,
                                float* scale, hipStream_t stream);
 
+// fp8 tokens and fp8 weights (both matmuls on the scaled fp8 MFMA).  act's
+// MX block scales take kA8ScalePitch bytes per act row (I / 32 of them used),
+// so I <= 32 * kA8ScalePitch; H and I are multiples of 128.
+constexpr int kA8ScalePitch = 32;
+
+// gate/up: xq [T, H] e4m3fn codes with xs [T] power-of-two scales; weight
+// codes and row scales as for the fp8-weight path; writes actq [rows, I]
+// codes and act_scales [rows, kA8ScalePitch] e8m0 bytes.  The counters must
+// be zero (the permutation's scan zeroes them).
+hipError_t launch_gemm_w13_a8(const Dims& d, const uint8_t* xq, const float* xs,
+                              const void* w13, const float* w13_scale, const void* shared_w13,
+                              const float* shared_w13_scale, const int32_t* offsets,
+                              const int32_t* sorted_rows, uint8_t* actq, uint8_t* act_scales,
+                              int* ctr, hipStream_t stream);
+
+// down: actq / act_scales as written above; y [rows, H] bf16 in slot order.
+hipError_t launch_gemm_w2_a8(const Dims& d, const uint8_t* actq, uint8_t* act_scales,
+                             const void* w2, const float* w2_scale, const void* shared_w2,
+                             const float* shared_w2_scale, const int32_t* offsets,
+                             const int32_t* sorted_rows, void* y, int* ctr, hipStream_t stream);
+
 hipError_t launch_combine(const Dims& d, const void* y, const int32_t* inv_rows,
                           const float* topk_w, void* out, hipStream_t stream);
 

@@ -21,7 +21,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 26, names
+    assert len(names) == 27, names
     assert set(names) == set(lbv.EXPORTS)
     L = ctypes.CDLL(lbv.LIB_PATH)
     for n in names:
@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert lbv.lbv_abi_version() == 5
+    assert lbv.lbv_abi_version() == 6
     texts = {lbv.lbv_status_string(s) for s in range(9)}
     assert len(texts) == 9
     assert lbv.lbv_status_string(99) == "unknown status"
@@ -388,6 +388,38 @@ def test_fp8_validation_paths():
     assert f(16, ws_bytes=need - 1) == lbv.LBV_ERR_WORKSPACE
     c0 = lbv.config(n_shared_experts=0)
     assert f(0, cfg=c0, w=lbv._Fp8WeightsC(A, B, A, B, None, None, None, None)) == lbv.LBV_OK
+
+
+def test_w8a8_validation_paths():
+    """lbv_moe_forward_w8a8 rejects before any launch: the fp32 config, H or I
+    not multiples of 128, I above 1024 (act's block scales take 32 bytes per
+    row), NULLs, alignment, overlap, a short workspace (the same size as
+    lbv_moe_forward's)."""
+    L = raw()
+    c = lbv.config()
+    W = lbv._Fp8WeightsC(A, B, A, B, A, B, A, B)
+    need = lbv.lbv_moe_workspace_size(c, 16)
+
+    def f(T, out=Cc, ws=BIG, ws_bytes=need, cfg=c, w=W):
+        return L.lbv_moe_forward_w8a8(ctypes.byref(cfg), T, A, None, A, B,
+                                      ctypes.byref(w) if w is not None else None, out, None, None,
+                                      ws, ws_bytes, None)
+    assert f(16, cfg=lbv.config(dtype="f32")) == lbv.LBV_ERR_UNSUPPORTED
+    assert f(16, cfg=lbv.config(hidden=2112)) == lbv.LBV_ERR_SHAPE
+    assert f(16, cfg=lbv.config(intermediate=704)) == lbv.LBV_ERR_SHAPE
+    assert f(16, cfg=lbv.config(intermediate=1152)) == lbv.LBV_ERR_SHAPE
+    assert f(16, cfg=lbv.config(intermediate=64)) == lbv.LBV_ERR_SHAPE
+    assert f(0, cfg=lbv.config(intermediate=64)) == lbv.LBV_ERR_SHAPE    # shape first
+    assert f(0) == lbv.LBV_OK
+    assert f(16, w=None) == lbv.LBV_ERR_NULL
+    assert f(16, w=lbv._Fp8WeightsC(A, None, A, B, A, B, A, B)) == lbv.LBV_ERR_NULL
+    assert f(16, w=lbv._Fp8WeightsC(A, B, A, B, A, B, A, None)) == lbv.LBV_ERR_NULL  # shared expert
+    assert f(16, w=lbv._Fp8WeightsC(A, B, A + 8, B, A, B, A, B)) == lbv.LBV_ERR_ALIGN
+    assert f(16, w=lbv._Fp8WeightsC(A, B, A, B + 2, A, B, A, B)) == lbv.LBV_ERR_ALIGN
+    assert f(16, out=A) == lbv.LBV_ERR_ALIAS
+    assert f(16, ws_bytes=need - 1) == lbv.LBV_ERR_WORKSPACE
+    assert f(16, cfg=lbv.config(intermediate=1024), ws_bytes=lbv.lbv_moe_workspace_size(
+        lbv.config(intermediate=1024), 16) - 1) == lbv.LBV_ERR_WORKSPACE   # I = 1024 is allowed
 
 
 def test_fp8_binding_shape_checks():
