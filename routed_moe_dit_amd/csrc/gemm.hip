@@ -223,8 +223,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     // writes.  The row scales are applied in the epilogues, the act block
     // scales by the MFMA.  A k-tile holds 128 values per row, so its rows are
     // 128 bytes, as a bf16 k-tile of 64: the same stages and copies.
-    static_assert(!A8 || (!W8 && !DENSE && (BM == 128 || BM == 192 || BM == 256) && NW == 8 && CWV == 4 && STG == 2),
-                  "fp8 tokens: 128-, 192- or 256-row tiles, 8 waves, 2 stages");
+    static_assert(!A8 || (!W8 && !DENSE && (BM == 64 || BM == 128 || BM == 192 || BM == 256) && NW == 8 && CWV == 4 && STG == 2),
+                  "fp8 tokens: 64- to 256-row tiles, 8 waves, 2 stages");
     // NW waves: 2 along the tokens x NW/2 along the weight rows (NW = 4: one
     // wave per SIMD with 128 x 128 accumulators; NW = 8: two per SIMD with
     // 128 x 64, so that one wave's MFMAs can cover the other's waits).
@@ -1476,8 +1476,13 @@ hipError_t launch_gemm_w13_a8(const Dims& d, const uint8_t* xq, const float* xs,
     a.kdim = d.H;
     a.ncols = d.I;
     a.ntn = (d.I + G1_BN / 2 - 1) / (G1_BN / 2);
-    hipLaunchKernelGGL((gemm_bf16_kernel<LBV_A8_BM, G1_BN, 0, 8, 4, LBV_G1_ORDER, 2, false, false, true>),
-                       dim3(cu_count() / 8 * 8), dim3(512), 0, stream, a);
+    // few rows per segment: 64-row tiles (as the bf16 path), else LBV_A8_BM
+    if (few_rows(d))
+        hipLaunchKernelGGL((gemm_bf16_kernel<64, G1_BN, 0, 8, 4, LBV_G1_ORDER, 2, false, false, true>),
+                           dim3(cu_count() / 8 * 8), dim3(512), 0, stream, a);
+    else
+        hipLaunchKernelGGL((gemm_bf16_kernel<LBV_A8_BM, G1_BN, 0, 8, 4, LBV_G1_ORDER, 2, false, false, true>),
+                           dim3(cu_count() / 8 * 8), dim3(512), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1499,8 +1504,12 @@ hipError_t launch_gemm_w2_a8(const Dims& d, const uint8_t* actq, uint8_t* act_sc
     a.kdim = d.I;
     a.ncols = d.H;
     a.ntn = (d.H + G2_BN - 1) / G2_BN;         // a partial last n-tile (H = 128 mod 256) is clamped
-    hipLaunchKernelGGL((gemm_bf16_kernel<LBV_A8_BM, G2_BN, 1, 8, 4, LBV_G2_ORDER, 2, false, false, true>),
-                       dim3(cu_count() / 8 * 8), dim3(512), 0, stream, a);
+    if (few_rows(d))
+        hipLaunchKernelGGL((gemm_bf16_kernel<64, G2_BN, 1, 8, 4, LBV_G2_ORDER, 2, false, false, true>),
+                           dim3(cu_count() / 8 * 8), dim3(512), 0, stream, a);
+    else
+        hipLaunchKernelGGL((gemm_bf16_kernel<LBV_A8_BM, G2_BN, 1, 8, 4, LBV_G2_ORDER, 2, false, false, true>),
+                           dim3(cu_count() / 8 * 8), dim3(512), 0, stream, a);
     return hipGetLastError();
 }
 

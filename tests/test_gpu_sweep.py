@@ -1,7 +1,8 @@
 """Seeded sweep of random small configurations through the C ABI, each against
 the CPU oracle on every token: the bf16 and fp32 block (experts, groups,
 top-k, shared experts, widths, token counts, padding), the block with fp8
-weights, and the attention kernel (samples, lengths, heads, masks).  Bars as
+weights, the block with fp8 weights and activations, and the attention
+kernel (samples, lengths, heads, masks).  Bars as
 in the per-step parity tests."""
 import numpy as np
 import pytest
@@ -14,6 +15,7 @@ from gpu_util import forward, note, upload
 from test_gpu_attention import bf16, check, u8, vt_of
 from test_gpu_fp8 import forward_fp8, oracle_dequantized
 from test_gpu_parity import check_forward
+from test_gpu_w8a8 import check_w8a8, forward_w8a8
 
 pytestmark = pytest.mark.gpu
 
@@ -76,6 +78,19 @@ def test_random_block_fp8_parity(wl):
     d = upload(wl, inp)
     out, ids, w = forward_fp8(wl, d)
     check_forward(wl, oracle_dequantized(inp), out, ids, w)
+
+
+A8_BLOCKS = [w for w in BLOCKS if w.dtype == "bf16" and w.hidden % 128 == 0 and
+             w.intermediate % 128 == 0]
+
+
+@pytest.mark.parametrize("wl", A8_BLOCKS, ids=lambda w: w.name)
+def test_random_block_w8a8_parity(wl):
+    note("sweep w8a8 forward %s" % wl.name)
+    inp = synth.make_inputs(wl)
+    d = upload(wl, inp)
+    out, ids, w = forward_w8a8(wl, d)
+    check_w8a8(wl, inp, oracle_dequantized(inp), out, ids, w)
 
 
 def random_attn(i):
