@@ -16,7 +16,11 @@ HBM.  Prints one JSON line:
     HBM when its algorithmic FLOP per byte is below the machine balance (few
     tokens: the weights stream once), else by the bf16 matrix cores;
   * router and permutation rates, the input digests, and the CPU oracle timed
-    on a bounded token sample on the host.
+    on a bounded token sample on the host;
+  * beside the headline (each leg on by default, --no-<leg> skips it): the FFN
+    half of a DiT layer with its AdaLN (adaln), the block with fp8 weights and
+    with fp8 weights and activations (fp8, w8a8), and the attention half of
+    the layer on the same token layout (attention_half).
 """
 import argparse
 import hashlib
@@ -47,13 +51,15 @@ def parse():
     p.add_argument("--cpu-sample", type=int, default=12000,
                    help="tokens of the same workload the CPU oracle is timed on")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--adaln", action="store_true",
+    # the legs beside the headline block (on by default; --no-adaln etc. skip them)
+    p.add_argument("--adaln", action=argparse.BooleanOptionalAction, default=True,
                    help="also time the FFN half of a DiT layer around the block "
                         "(lbv_moe_ffn_adaln, token-level temb6) and its AdaLN kernel alone")
-    p.add_argument("--fp8", action="store_true",
+    p.add_argument("--fp8", action=argparse.BooleanOptionalAction, default=True,
                    help="also time the block with fp8 (e4m3fn, per-row power-of-two scale) "
-                        "expert weights (lbv_moe_forward_fp8) and the device quantizer")
-    p.add_argument("--attn", action="store_true",
+                        "expert weights (lbv_moe_forward_fp8), the device quantizer, and the "
+                        "block with fp8 weights and fp8 activations (lbv_moe_forward_w8a8)")
+    p.add_argument("--attn", action=argparse.BooleanOptionalAction, default=True,
                    help="also time the attention half of the layer (lbv_attn_forward) on the "
                         "attention workload of the same token layout, and its kernels")
     p.add_argument("--copy-calibration", action="store_true",
