@@ -61,7 +61,7 @@ def edge_rows(cols, rng):
     return np.array(rows)
 
 
-@pytest.mark.parametrize("cols", [16, 80, 768, 2048, 2112])
+@pytest.mark.parametrize("cols", [16, 80, 768, 2048, 2112, 4096, 4112])
 @pytest.mark.parametrize("src", ["bf16", "f32"])
 def test_quantize_bit_exact(cols, src):
     note("quantize cols=%d src=%s" % (cols, src))
