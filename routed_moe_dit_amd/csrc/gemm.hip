@@ -1270,8 +1270,12 @@ __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
         }
     }
     const char* y = static_cast<const char*>(a.y);
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
     for (int h0 = lane * EPL; h0 < a.H; h0 += 64 * EPL * NC) {
         u32x4 q[NC][MAXS];
+        // RESID: the residual row and both gate parts are loaded with the
+        // slot rows, so that all of a step's loads are in flight together
+        f32x4 xv[NC][EPL / 4], ga[NC][EPL / 4], gb[NC][EPL / 4];
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const int h = h0 + c * 64 * EPL;
@@ -1281,6 +1285,20 @@ __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
                     const int r = rows[k] < 0 ? 0 : rows[k];   // unused when the slot is empty
                     const u32x4* src = reinterpret_cast<const u32x4*>(y + (static_cast<int64_t>(r) * a.H + h) * ESZ);
                     q[c][k] = LBV_COMB_NT ? __builtin_nontemporal_load(src) : *src;
+                }
+            }
+            if constexpr (RESID) {
+                if (h < a.H) {
+                    const f32x4* xr = reinterpret_cast<const f32x4*>(a.x + t * a.H + h);
+                    const f32x4* g0 = reinterpret_cast<const f32x4*>(a.table + 5 * a.H + h);
+                    const f32x4* g1 = reinterpret_cast<const f32x4*>(a.temb + t * a.temb_stride + 5 * a.H + h);
+#pragma unroll
+                    for (int j = 0; j < EPL / 4; ++j) {
+                        xv[c][j] = __builtin_nontemporal_load(xr + j);
+                        ga[c][j] = g0[j];
+                        // one row for every token when the stride is 0: keep it cached
+                        gb[c][j] = a.temb_stride ? __builtin_nontemporal_load(g1 + j) : g1[j];
+                    }
                 }
             }
         }
@@ -1296,29 +1314,26 @@ __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
                 if (k < a.KS && rows[k] >= 0) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
+                        // one fma per slot, written out (the compiler forms
+                        // the same fma from a * b + c; explicit, the order of
+                        // roundings does not depend on its choice)
                         if (BF16) {
-                            acc[2 * i] += wt[k] * __uint_as_float(q[c][k][i] << 16);
-                            acc[2 * i + 1] += wt[k] * __uint_as_float(q[c][k][i] & 0xffff0000u);
+                            acc[2 * i] = __builtin_fmaf(wt[k], __uint_as_float(q[c][k][i] << 16), acc[2 * i]);
+                            acc[2 * i + 1] = __builtin_fmaf(wt[k], __uint_as_float(q[c][k][i] & 0xffff0000u), acc[2 * i + 1]);
                         } else {
-                            acc[i] += wt[k] * __uint_as_float(q[c][k][i]);
+                            acc[i] = __builtin_fmaf(wt[k], __uint_as_float(q[c][k][i]), acc[i]);
                         }
                     }
                 }
             }
             if constexpr (RESID) {
-                typedef float f32x4 __attribute__((ext_vector_type(4)));
-                const float* xr = a.x + t * a.H + h;
-                const float* g0 = a.table + 5 * a.H + h;
-                const float* g1 = a.temb + t * a.temb_stride + 5 * a.H + h;
                 float* orow = static_cast<float*>(a.out) + t * a.H + h;
 #pragma unroll
                 for (int j = 0; j < EPL / 4; ++j) {
-                    const f32x4 xv = *reinterpret_cast<const f32x4*>(xr + 4 * j);
-                    const f32x4 ga = *reinterpret_cast<const f32x4*>(g0 + 4 * j);
-                    const f32x4 gb = *reinterpret_cast<const f32x4*>(g1 + 4 * j);
                     f32x4 ov;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) ov[i] = xv[i] + (ga[i] + gb[i]) * acc[4 * j + i];
+                    for (int i = 0; i < 4; ++i)
+                        ov[i] = xv[c][j][i] + (ga[c][j][i] + gb[c][j][i]) * acc[4 * j + i];
                     __builtin_nontemporal_store(ov, reinterpret_cast<f32x4*>(orow + 4 * j));
                 }
             } else {
