@@ -48,8 +48,11 @@
 // G*_WAVES: waves per workgroup (4 or 8); G*_COPY_WAVES: waves that issue
 // the stage copies; G*_ORDER: m-tiles per block of the tile order (1: m-tile
 // major, the n-tiles of an m-tile adjacent; large: n-tile major inside each
-// segment); FEW_ROWS / FEW_STAGES: below FEW_ROWS rows per segment on average
-// the matmuls use 64-row tiles with a FEW_STAGES-deep ring.
+// segment); SMALL_ROWS (W8_SMALL_ROWS with fp8 weights) / MID_ROWS /
+// FEW_STAGES: below SMALL_ROWS rows per segment on average the bf16-token
+// matmuls use 64-row tiles, below MID_ROWS 128-row tiles, both with a
+// FEW_STAGES-deep ring; A8_SMALL_ROWS / A8_MID_ROWS: the same for the
+// fp8-token matmuls (two stages, A8_BM rows above).
 #ifndef LBV_NPRE
 #define LBV_NPRE 8
 #endif
@@ -86,8 +89,20 @@
 #ifndef LBV_G2_ORDER
 #define LBV_G2_ORDER 1024
 #endif
-#ifndef LBV_FEW_ROWS
-#define LBV_FEW_ROWS 256
+#ifndef LBV_SMALL_ROWS
+#define LBV_SMALL_ROWS 20
+#endif
+#ifndef LBV_W8_SMALL_ROWS
+#define LBV_W8_SMALL_ROWS 80
+#endif
+#ifndef LBV_MID_ROWS
+#define LBV_MID_ROWS 480
+#endif
+#ifndef LBV_A8_SMALL_ROWS
+#define LBV_A8_SMALL_ROWS 40
+#endif
+#ifndef LBV_A8_MID_ROWS
+#define LBV_A8_MID_ROWS 80
 #endif
 #ifndef LBV_FEW_STAGES
 #define LBV_FEW_STAGES 3
@@ -1367,12 +1382,29 @@ GemmArgs make_args(const Dims& d) {
     return a;
 }
 
-// Few rows per segment on average (T (K + ns) / S < LBV_FEW_ROWS): the
-// matmuls use 64-row tiles, whose copies and MFMAs are a quarter of a
-// 256-row tile's for the A side, instead of padding each expert's few rows
-// to 256.
-bool few_rows(const Dims& d) {
-    return d.T * d.KS < static_cast<int64_t>(LBV_FEW_ROWS) * d.S;
+// Tile height of the grouped matmuls, from the rows per segment on average,
+// T (K + ns) / S: 64 below `small`, 128 below `mid`, else `big`.  Shorter
+// tiles pad each expert's few rows less; taller ones send each weight slice
+// through a CU's copy path fewer times (128-row tiles hold a segment in about
+// half as many tiles as 64-row ones).  With bf16 tokens the 64- and 128-row
+// tiles have three stages (3 x 48 KB of LDS at 128 rows), which the
+// HBM-bound small batches need, and 256-row tiles two.  The thresholds come
+// from sweeps of the 128-expert layer (H 2048, I 768, top-8, one shared
+// expert) over 50 to 38,000 tokens, forwards timed per tile height:
+//   bf16 weights: 64 rows lead by ~1.5% up to 200 tokens (~14 rows per
+//     segment), 128 rows from 400 to 6,000 tokens (28-420 rows; 1-14% ahead
+//     of the better of the other two), 256 rows from 8,000 tokens (560 rows);
+//   fp8 weights: 64 rows lead by ~1.5% at 800 tokens (56 rows), 128 rows by
+//     9-12% at 1,600 and 3,000 tokens;
+//   fp8 tokens (64, 128, 192 rows, two stages): 64 rows up to 400 tokens
+//     (28 rows), 128 rows at 800 tokens (56 rows, 4% ahead), 192 rows from
+//     1,600 tokens (112 rows; 12-19% ahead of 64 rows at 1,600 and 3,000).
+// A row's sums do not depend on the tile height (same k order), so neither
+// does the result.
+int tile_rows(const Dims& d, int small, int mid, int big) {
+    const int64_t rows = d.T * d.KS;
+    if (rows < static_cast<int64_t>(small) * d.S) return 64;
+    return rows < static_cast<int64_t>(mid) * d.S ? 128 : big;
 }
 
 // Zeroes the tile queue counters ahead of a grouped matmul on the same stream
@@ -1387,8 +1419,12 @@ int64_t max_mtiles(const Dims& d, int BM) {
 
 template <bool W8>
 void launch_w13_bf16(const Dims& d, const GemmArgs& a, hipStream_t stream) {
-    if (few_rows(d))
+    const int bm = tile_rows(d, W8 ? LBV_W8_SMALL_ROWS : LBV_SMALL_ROWS, LBV_MID_ROWS, 256);
+    if (bm == 64)
         hipLaunchKernelGGL((gemm_bf16_kernel<64, G1_BN, 0, LBV_G1_WAVES, LBV_G1_COPY_WAVES, LBV_G1_ORDER, LBV_FEW_STAGES, W8, false>),
+                           dim3(cu_count() / 8 * 8), dim3(LBV_G1_WAVES * 64), 0, stream, a);
+    else if (bm == 128)
+        hipLaunchKernelGGL((gemm_bf16_kernel<128, G1_BN, 0, LBV_G1_WAVES, LBV_G1_COPY_WAVES, LBV_G1_ORDER, LBV_FEW_STAGES, W8, false>),
                            dim3(cu_count() / 8 * 8), dim3(LBV_G1_WAVES * 64), 0, stream, a);
     else
         hipLaunchKernelGGL((gemm_bf16_kernel<G1_BM, G1_BN, 0, LBV_G1_WAVES, LBV_G1_COPY_WAVES, LBV_G1_ORDER, 2, W8, false>),
@@ -1397,8 +1433,12 @@ void launch_w13_bf16(const Dims& d, const GemmArgs& a, hipStream_t stream) {
 
 template <bool W8>
 void launch_w2_bf16(const Dims& d, const GemmArgs& a, hipStream_t stream) {
-    if (few_rows(d))
+    const int bm = tile_rows(d, W8 ? LBV_W8_SMALL_ROWS : LBV_SMALL_ROWS, LBV_MID_ROWS, 256);
+    if (bm == 64)
         hipLaunchKernelGGL((gemm_bf16_kernel<64, G2_BN, 1, LBV_G2_WAVES, LBV_G2_COPY_WAVES, LBV_G2_ORDER, LBV_FEW_STAGES, W8, false>),
+                           dim3(cu_count() / 8 * 8), dim3(LBV_G2_WAVES * 64), 0, stream, a);
+    else if (bm == 128)
+        hipLaunchKernelGGL((gemm_bf16_kernel<128, G2_BN, 1, LBV_G2_WAVES, LBV_G2_COPY_WAVES, LBV_G2_ORDER, LBV_FEW_STAGES, W8, false>),
                            dim3(cu_count() / 8 * 8), dim3(LBV_G2_WAVES * 64), 0, stream, a);
     else
         hipLaunchKernelGGL((gemm_bf16_kernel<G2_BM, G2_BN, 1, LBV_G2_WAVES, LBV_G2_COPY_WAVES, LBV_G2_ORDER, 2, W8, false>),
@@ -1491,9 +1531,12 @@ hipError_t launch_gemm_w13_a8(const Dims& d, const uint8_t* xq, const float* xs,
     a.kdim = d.H;
     a.ncols = d.I;
     a.ntn = (d.I + G1_BN / 2 - 1) / (G1_BN / 2);
-    // few rows per segment: 64-row tiles (as the bf16 path), else LBV_A8_BM
-    if (few_rows(d))
+    const int bm = tile_rows(d, LBV_A8_SMALL_ROWS, LBV_A8_MID_ROWS, LBV_A8_BM);
+    if (bm == 64)
         hipLaunchKernelGGL((gemm_bf16_kernel<64, G1_BN, 0, 8, 4, LBV_G1_ORDER, 2, false, false, true>),
+                           dim3(cu_count() / 8 * 8), dim3(512), 0, stream, a);
+    else if (bm == 128)
+        hipLaunchKernelGGL((gemm_bf16_kernel<128, G1_BN, 0, 8, 4, LBV_G1_ORDER, 2, false, false, true>),
                            dim3(cu_count() / 8 * 8), dim3(512), 0, stream, a);
     else
         hipLaunchKernelGGL((gemm_bf16_kernel<LBV_A8_BM, G1_BN, 0, 8, 4, LBV_G1_ORDER, 2, false, false, true>),
@@ -1519,8 +1562,12 @@ hipError_t launch_gemm_w2_a8(const Dims& d, const uint8_t* actq, uint8_t* act_sc
     a.kdim = d.I;
     a.ncols = d.H;
     a.ntn = (d.H + G2_BN - 1) / G2_BN;         // a partial last n-tile (H = 128 mod 256) is clamped
-    if (few_rows(d))
+    const int bm = tile_rows(d, LBV_A8_SMALL_ROWS, LBV_A8_MID_ROWS, LBV_A8_BM);
+    if (bm == 64)
         hipLaunchKernelGGL((gemm_bf16_kernel<64, G2_BN, 1, 8, 4, LBV_G2_ORDER, 2, false, false, true>),
+                           dim3(cu_count() / 8 * 8), dim3(512), 0, stream, a);
+    else if (bm == 128)
+        hipLaunchKernelGGL((gemm_bf16_kernel<128, G2_BN, 1, 8, 4, LBV_G2_ORDER, 2, false, false, true>),
                            dim3(cu_count() / 8 * 8), dim3(512), 0, stream, a);
     else
         hipLaunchKernelGGL((gemm_bf16_kernel<LBV_A8_BM, G2_BN, 1, 8, 4, LBV_G2_ORDER, 2, false, false, true>),

@@ -120,11 +120,13 @@ FP8_CASES = [
     var("ns2", n_shared=2, T=64),
     var("T1", T=1),
     var("E128_K12_ns2", num_experts=128, top_k=12, n_shared=2, T=300, hidden=256),
-    # 256-row tiles (54,000 rows) at the LingBot dims
+    # 128-row tiles (419 rows per segment) and 256-row tiles (558) at the LingBot dims
     var("E128_T6000_full_dims", num_experts=128, top_k=8, T=6000, hidden=2048, intermediate=768),
-    # odd k-tile counts and partial n-tiles, 64-row and 256-row tiles
+    var("E128_T8000_full_dims", num_experts=128, top_k=8, T=8000, hidden=2048, intermediate=768),
+    # odd k-tile counts and partial n-tiles with 64-, 128- and 256-row tiles
+    var("odd_H2112_I704_T200", num_experts=128, top_k=8, T=200, hidden=2112, intermediate=704),
     var("odd_H2112_I704_T500", num_experts=128, top_k=8, T=500, hidden=2112, intermediate=704),
-    var("odd_H2112_I704_T3000", num_experts=128, top_k=8, T=3000, hidden=2112, intermediate=704),
+    var("odd_H2112_I704_T8000", num_experts=128, top_k=8, T=8000, hidden=2112, intermediate=704),
 ]
 
 

@@ -164,14 +164,23 @@ def test_permute_parity(T, E, K, ns):
 
 
 
+# The bf16 matmuls pick their tile height from the rows per segment on
+# average, T (K + ns) / (E + ns): 64 rows below 20, 128 rows below 480, else
+# 256 rows.  The cases cover each height at the LingBot dims and with odd dims.
 GEMM_CASES = [
-    W[0], W[1], var("ns2_ragged", n_shared=2, T=77),
-    # 54,000 rows: past the few-rows switch, so the 256-row kernels run
+    W[0],
+    W[1],                                                          # 128-row tiles (56 rows)
+    var("ns2_ragged", n_shared=2, T=77),                           # 64-row tiles (9 rows)
+    # 54,000 rows, several 128-row tiles per segment (419 rows)
     var("E128_T6000_full_dims", num_experts=128, top_k=8, T=6000, hidden=2048, intermediate=768),
+    # 72,000 rows: 256-row tiles (558 rows)
+    var("E128_T8000_full_dims", num_experts=128, top_k=8, T=8000, hidden=2048, intermediate=768),
     # an odd number of 64-wide k-tiles on both matmuls (H/64 = 33, I/64 = 11)
-    # and partial n-tiles (I/128 = 5.5, H/256 = 8.25), with 256-row and 64-row tiles
+    # and partial n-tiles (I/128 = 5.5, H/256 = 8.25), with 256-, 128- and 64-row tiles
+    var("odd_H2112_I704_T8000", num_experts=128, top_k=8, T=8000, hidden=2112, intermediate=704),
     var("odd_H2112_I704_T3000", num_experts=128, top_k=8, T=3000, hidden=2112, intermediate=704),
     var("odd_H2112_I704_T500", num_experts=128, top_k=8, T=500, hidden=2112, intermediate=704),
+    var("odd_H2112_I704_T200", num_experts=128, top_k=8, T=200, hidden=2112, intermediate=704),
 ]
 
 
@@ -306,9 +315,9 @@ def test_forward_parity(wl):
 
 @pytest.mark.timeout(600)
 def test_forward_parity_mid_size():
-    """6,000 tokens (past the router's 4096-token switch, 256-row matmul
-    tiles): every token against the oracle."""
-    wl = var("E128_T6000", num_experts=128, top_k=8, T=6000, hidden=256, intermediate=256)
+    """8,000 tokens (past the router's 4096-token switch; 558 rows per
+    segment, so 256-row matmul tiles): every token against the oracle."""
+    wl = var("E128_T8000", num_experts=128, top_k=8, T=8000, hidden=256, intermediate=256)
     note("forward %s" % wl.name)
     inp = synth.make_inputs(wl)
     d = upload(wl, inp)

@@ -82,8 +82,10 @@ CASES = [
     var("T1", T=1),
     var("E128_K12_ns2", num_experts=128, top_k=12, n_shared=2, T=300, hidden=256),
     var("I1024", T=300, hidden=256, intermediate=1024),
-    # odd k-tile counts (17 along H, 5 along I: a zero-filled stage)
+    # odd k-tile counts (17 along H, 5 along I: a zero-filled stage), with
+    # 64-row (35 rows per segment) and 128-row tiles (70 rows)
     var("odd_H2176_I640", num_experts=128, top_k=8, T=500, hidden=2176, intermediate=640),
+    var("odd_H2176_I640_T1000", num_experts=128, top_k=8, T=1000, hidden=2176, intermediate=640),
     # many 192-row tiles per expert at the LingBot dims
     var("E128_T6000_full_dims", num_experts=128, top_k=8, T=6000, hidden=2048, intermediate=768),
 ]
