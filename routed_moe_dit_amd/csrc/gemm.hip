@@ -48,8 +48,8 @@
 // G*_WAVES: waves per workgroup (4 or 8); G*_COPY_WAVES: waves that issue
 // the stage copies; G*_ORDER: m-tiles per block of the tile order (1: m-tile
 // major, the n-tiles of an m-tile adjacent; large: n-tile major inside each
-// segment); SMALL_ROWS (W8_SMALL_ROWS with fp8 weights) / MID_ROWS /
-// FEW_STAGES: below SMALL_ROWS rows per segment on average the bf16-token
+// segment); G*_SMALL_ROWS (W8_G*_SMALL_ROWS with fp8 weights) / MID_ROWS /
+// FEW_STAGES: below G*_SMALL_ROWS rows per segment on average the bf16-token
 // matmuls use 64-row tiles, below MID_ROWS 128-row tiles, both with a
 // FEW_STAGES-deep ring; A8_SMALL_ROWS / A8_MID_ROWS: the same for the
 // fp8-token matmuls (two stages, A8_BM rows above).
@@ -89,11 +89,17 @@
 #ifndef LBV_G2_ORDER
 #define LBV_G2_ORDER 1024
 #endif
-#ifndef LBV_SMALL_ROWS
-#define LBV_SMALL_ROWS 20
+#ifndef LBV_G1_SMALL_ROWS
+#define LBV_G1_SMALL_ROWS 20
 #endif
-#ifndef LBV_W8_SMALL_ROWS
-#define LBV_W8_SMALL_ROWS 80
+#ifndef LBV_G2_SMALL_ROWS
+#define LBV_G2_SMALL_ROWS 20
+#endif
+#ifndef LBV_W8_G1_SMALL_ROWS
+#define LBV_W8_G1_SMALL_ROWS 80
+#endif
+#ifndef LBV_W8_G2_SMALL_ROWS
+#define LBV_W8_G2_SMALL_ROWS 20
 #endif
 #ifndef LBV_MID_ROWS
 #define LBV_MID_ROWS 480
@@ -1394,8 +1400,9 @@ GemmArgs make_args(const Dims& d) {
 //   bf16 weights: 64 rows lead by ~1.5% up to 200 tokens (~14 rows per
 //     segment), 128 rows from 400 to 6,000 tokens (28-420 rows; 1-14% ahead
 //     of the better of the other two), 256 rows from 8,000 tokens (560 rows);
-//   fp8 weights: 64 rows lead by ~1.5% at 800 tokens (56 rows), 128 rows by
-//     9-12% at 1,600 and 3,000 tokens;
+//   fp8 weights: 64-row gate/up tiles with 128-row down tiles lead by ~2%
+//     from 600 to 1,000 tokens (42-70 rows), 128 rows for both by 9-12% at
+//     1,600 and 3,000 tokens;
 //   fp8 tokens (64, 128, 192 rows, two stages): 64 rows up to 400 tokens
 //     (28 rows), 128 rows at 800 tokens (56 rows, 4% ahead), 192 rows from
 //     1,600 tokens (112 rows; 12-19% ahead of 64 rows at 1,600 and 3,000).
@@ -1419,7 +1426,7 @@ int64_t max_mtiles(const Dims& d, int BM) {
 
 template <bool W8>
 void launch_w13_bf16(const Dims& d, const GemmArgs& a, hipStream_t stream) {
-    const int bm = tile_rows(d, W8 ? LBV_W8_SMALL_ROWS : LBV_SMALL_ROWS, LBV_MID_ROWS, 256);
+    const int bm = tile_rows(d, W8 ? LBV_W8_G1_SMALL_ROWS : LBV_G1_SMALL_ROWS, LBV_MID_ROWS, 256);
     if (bm == 64)
         hipLaunchKernelGGL((gemm_bf16_kernel<64, G1_BN, 0, LBV_G1_WAVES, LBV_G1_COPY_WAVES, LBV_G1_ORDER, LBV_FEW_STAGES, W8, false>),
                            dim3(cu_count() / 8 * 8), dim3(LBV_G1_WAVES * 64), 0, stream, a);
@@ -1433,7 +1440,7 @@ void launch_w13_bf16(const Dims& d, const GemmArgs& a, hipStream_t stream) {
 
 template <bool W8>
 void launch_w2_bf16(const Dims& d, const GemmArgs& a, hipStream_t stream) {
-    const int bm = tile_rows(d, W8 ? LBV_W8_SMALL_ROWS : LBV_SMALL_ROWS, LBV_MID_ROWS, 256);
+    const int bm = tile_rows(d, W8 ? LBV_W8_G2_SMALL_ROWS : LBV_G2_SMALL_ROWS, LBV_MID_ROWS, 256);
     if (bm == 64)
         hipLaunchKernelGGL((gemm_bf16_kernel<64, G2_BN, 1, LBV_G2_WAVES, LBV_G2_COPY_WAVES, LBV_G2_ORDER, LBV_FEW_STAGES, W8, false>),
                            dim3(cu_count() / 8 * 8), dim3(LBV_G2_WAVES * 64), 0, stream, a);
